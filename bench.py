@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark: effective HBM bandwidth of the masked causal conv1d backward (fused gradX + gradWeight)
+on one MI355X, for the workload S=16384, B=32 (B*S = 512K), H=5120, bf16, Bernoulli(0.9) mask.
+
+A step is one mccb_backward call (the fused mask + gradX + gradWeight-partials kernel and the
+fixed-order gradWeight reduction) over inputs already resident in HBM. Effective GB/s counts the
+bytes the method must move: read gradY and x, write gradX (2 bytes each per element), read the mask
+(1 byte per (j,i)), read the weight and write gradWeight; workspace traffic is not counted.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "effective HBM GB/s (and % of peak) for fused gradX+gradWeight, B*S=512K H=5120"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_ceiling(torch, device, nbytes: int = 4 << 30, reps: int = 10) -> float:
+    """GB/s (read + write) of torch's device-to-device copy, a plain streaming reference."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
+
+
+def cpu_baseline(wl, gy, x, w, m, seconds: float, rows_per_chunk: int = 64) -> dict:
+    """Time the CPU fp64 oracle on consecutive row chunks of the same inputs until `seconds` of
+    compute have run. Chunk copies to the host and input decoding set-up are not timed; the
+    oracle's own decode + compute + encode is."""
+    import oracle
+    from synth import workloads as wls
+
+    orc = oracle.get()
+    w16 = wls.bits(w)
+    elapsed, elems, chunks = 0.0, 0, 0
+    r = 0
+    while elapsed < seconds and r < wl.S:
+        r1 = min(r + rows_per_chunk, wl.S)
+        gyc, xc = wls.bits(gy[r:r1]), wls.bits(x[r:r1])
+        mc = None if m is None else m[:, r:r1].cpu().numpy()
+        t0 = time.perf_counter()
+        orc.backward(wl.dtype, gyc, xc, w16, mc, want_gx64=False)
+        elapsed += time.perf_counter() - t0
+        elems += (r1 - r) * wl.B * wl.H
+        chunks += 1
+        r = r1
+    rows = r
+    alg = 3 * elems * 2 + (rows * wl.B if m is not None else 0) + chunks * 2 * 3 * wl.H * 2
+    return {
+        "value": round(alg / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": (f"rows 0..{rows - 1} of the workload in {chunks} independent chunks of "
+                   f"{rows_per_chunk} rows (x B={wl.B} x H={wl.H}), {elapsed:.1f} s of oracle time"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=None,
+                    help="index into synth.WORKLOADS (default: the B*S=512K H=5120 workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the method needs no cross-GPU communication on "
+              "this build's single-GPU boxes; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import masked_depthwise_causal_amd as mdc
+    from synth import HEADLINE, WORKLOADS
+    from synth import workloads as wls
+
+    wl = WORKLOADS[HEADLINE if args.workload is None else args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {wl.name}: {wl.describe()}")
+    gy = wls.full_tensor(wl, wls.STREAM_GY, dev)
+    x = wls.full_tensor(wl, wls.STREAM_X, dev)
+    w = wls.weight_tensor(wl, dev)
+    m = wls.mask_tensor(wl, dev)
+    gx = torch.empty_like(gy)
+    gw = torch.empty_like(w)
+    ws = mdc.workspace_for(wl.S, wl.B, wl.H, gy.dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    log("inputs resident")
+
+    def step():
+        mdc.backward(gy, x, w, m, gradX=gx, gradWeight=gw, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    mdc.mccb_profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms, reduce_ms, n_prof = mdc.mccb_profile_end()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+
+    alg = wl.algorithmic_bytes()
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    # dominant kernel: the fused pass moves everything except the gradWeight write
+    fused_alg = alg - 3 * wl.H * 2
+    fused_avg_ms = fused_ms / max(n_prof, 1)
+    achieved = fused_alg / (fused_avg_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "mccb_fused_bwd", "avg_ms": round(fused_avg_ms, 5),
+                "reduce_avg_ms": round(reduce_ms / max(n_prof, 1), 5)}
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = round(copy_ceiling(torch, dev), 1)
+        log(f"copy ceiling {ceiling} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, gy, x, w, m, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.describe(), "S": wl.S, "B": wl.B, "H": wl.H,
+                   "algorithmic_bytes": alg, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "copy_ceiling_gbs": ceiling},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,132 @@
+/*
+ * mccb.h -- masked causal depthwise conv1d backward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one documented on the page "aclnnMaskedCausalConv1dBackward" (Ascend CANN
+ * aclnn operator), section 功能说明 (function description). With gradY, x and gradX of shape
+ * [S,B,H], weight and gradWeight of shape [W=3,H] and an optional bool mask of shape [B,S]:
+ *
+ *   gradYMasked[i,j] = mask[j,i] * gradY[i,j]
+ *   gradX[i,j]       = sum_{k=0}^{2} gradYMasked[i+k, j] * weight[2-k]
+ *   gradWeight[k]    = sum_{j=0}^{B-1} sum_{i=0}^{S-1} gradYMasked[i+2-k, j] * x[i,j]
+ *
+ * Rows past the end (i' >= S) are zero. Every operation is independent per channel h (the
+ * equations leave h implicit). The window W is fixed at 3 (constraints section), so the API has no
+ * W argument.
+ *
+ * The interface keeps the page's two-phase shape (function prototype section): a first call that
+ * validates the arguments and reports the device workspace size, and a second call that enqueues
+ * the computation on a stream. There is no executor object: the second call takes the tensors
+ * again and re-validates them.
+ *
+ * Tensors are raw device pointers to contiguous row-major storage:
+ *   gradY, x, gradX : [S,B,H], element (i,j,h) at (i*B + j)*H + h
+ *   weight          : [3,H],   element (k,h)   at k*H + h
+ *   gradWeight      : [3,H]
+ *   mask            : [B,S] one byte per element, element (j,i) at j*S + i, nonzero = true (keep);
+ *                     NULL means every position is kept (the page's default for the optional mask).
+ * All five floating-point tensors share one dtype, bfloat16 or float16 (parameter table).
+ *
+ * Results: gradX is written once, correctly rounded (round to nearest, ties to even) from the exact
+ * three-term sum. gradWeight is accumulated in fp32 partials and reduced in fp64 in a fixed order,
+ * then rounded to the dtype, so repeated calls with the same inputs give bit-identical outputs
+ * (constraints section: deterministic by default). Both outputs are overwritten, never accumulated.
+ *
+ * Preconditions that are NOT checked (constraints section): inputs contain no inf or NaN, and
+ * neither inputs nor intermediate results exceed the range of the dtype.
+ */
+#ifndef MCCB_H
+#define MCCB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of gradY, x, weight, gradX and gradWeight (parameter table: BFLOAT16, FLOAT16). */
+typedef enum { MCCB_BF16 = 0, MCCB_FP16 = 1 } mccb_dtype_t;
+
+/* Status codes. The first three take the numbers of the page's return-code table (section 返回值)
+ * for the same three error classes. */
+enum {
+    MCCB_OK = 0,
+    /* a required pointer (input, output, out-parameter, or a workspace that is needed) is NULL */
+    MCCB_ERR_PARAM_NULLPTR = 161001,
+    /* dtype out of range, misaligned pointer, overlapping buffers, workspace too small */
+    MCCB_ERR_PARAM_INVALID = 161002,
+    /* shape out of the supported range: B in [1,32], S >= 1, B*S in [1, 524288],
+     * H in [384, 24576] and H % 64 == 0 (constraints section) */
+    MCCB_ERR_SHAPE = 561002,
+    /* a HIP runtime call or kernel launch failed (the page names no code for this) */
+    MCCB_ERR_RUNTIME = -1
+};
+
+/*
+ * Phase 1 (the page's ...GetWorkspaceSize). Validates the shape and dtype and stores in
+ * *workspace_size the number of device bytes the caller must provide to mccb_backward for this
+ * (S, B, H, dtype). The size depends on nothing else. Host-only; makes no HIP call.
+ * Returns MCCB_OK, MCCB_ERR_PARAM_NULLPTR (workspace_size NULL), MCCB_ERR_PARAM_INVALID (dtype)
+ * or MCCB_ERR_SHAPE.
+ */
+int mccb_get_workspace_size(int64_t S, int64_t B, int64_t H, int dtype, uint64_t *workspace_size);
+
+/*
+ * Phase 2 (the page's second call). Enqueues the backward on `stream` (a hipStream_t; NULL = the
+ * default stream) and returns without waiting; the caller synchronizes the stream before reading
+ * gradX or gradWeight.
+ *
+ *   gradY, x, weight : inputs, device memory, 16-byte aligned, not modified
+ *   mask             : optional input, device memory, any alignment, or NULL (= all true)
+ *   gradX, gradWeight: outputs, device memory, 16-byte aligned, overwritten
+ *   workspace        : device scratch of at least the phase-1 size, 16-byte aligned, owned by the
+ *                      caller (may be NULL only when the phase-1 size is 0). Its contents need no
+ *                      initialisation and are meaningless afterwards. It must not be used by
+ *                      another call that is in flight at the same time.
+ *
+ * The library allocates nothing and keeps no state between calls (apart from the optional
+ * profiling record below). gradX must not overlap gradY or x; no output or the workspace may
+ * overlap any other buffer.
+ *
+ * Validation happens on the host before any HIP call, in this order: NULL pointers
+ * (MCCB_ERR_PARAM_NULLPTR), dtype (MCCB_ERR_PARAM_INVALID), shape (MCCB_ERR_SHAPE), workspace,
+ * alignment and overlap (MCCB_ERR_PARAM_INVALID / MCCB_ERR_PARAM_NULLPTR). On any error nothing is
+ * enqueued. MCCB_ERR_RUNTIME reports a failed kernel launch.
+ */
+int mccb_backward(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                  void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
+                  void *workspace, uint64_t workspace_size, void *stream);
+
+/* The tiling chosen for a shape; a pure function of (S, B, H, dtype). Exposed so that tests can
+ * place edge cases on tile boundaries. */
+typedef struct {
+    int64_t rows_per_wave;   /* rows of [S, B*H] one wavefront walks */
+    int64_t rows_per_strip;  /* rows per fused-kernel block (waves_per_block * rows_per_wave) */
+    int64_t n_strips;        /* ceil(S / rows_per_strip) */
+    int64_t cols_per_block;  /* columns of [S, B*H] one fused-kernel block covers */
+    int64_t n_col_blocks;    /* ceil(B*H / cols_per_block) */
+    int64_t waves_per_block;
+    uint64_t workspace_size; /* same value as mccb_get_workspace_size */
+} mccb_plan_t;
+
+/* Fills *plan for a valid shape. Same return codes as mccb_get_workspace_size. Host-only. */
+int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *mccb_status_string(int status);
+
+/*
+ * Optional per-kernel timing, for benchmarks. After mccb_profile_begin(n), each of the next n
+ * mccb_backward calls records HIP events on its stream around its two kernels (the fused
+ * mask/gradX/gradWeight-partials kernel and the gradWeight reduction). mccb_profile_end waits for
+ * the recorded events, returns the summed milliseconds of each kernel and the number of calls
+ * recorded, and turns recording off. Returns MCCB_OK or MCCB_ERR_RUNTIME. Not thread-safe with
+ * respect to concurrent mccb_backward calls.
+ */
+int mccb_profile_begin(int max_calls);
+int mccb_profile_end(double *fused_ms, double *reduce_ms, int *calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCCB_H */

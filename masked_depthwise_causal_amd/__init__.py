@@ -1,0 +1,129 @@
+"""Masked causal depthwise conv1d backward on MI355X (gfx950).
+
+Python binding over the C-ABI of ``libmccb.so`` (``include/mccb.h``). This layer only marshals
+arguments: every step of the computation runs in the library's HIP kernels. PyTorch is used for
+device memory and streams.
+
+The operation is the one on the page "aclnnMaskedCausalConv1dBackward", section 功能说明
+(function description): gradX and gradWeight of a depthwise causal conv1d over [S,B,H] tensors with a
+[3,H] weight and an optional [B,S] bool mask.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import MccbError, Plan, lib, status_string  # noqa: F401
+
+MCCB_BF16, MCCB_FP16 = 0, 1
+MCCB_OK = 0
+MCCB_ERR_PARAM_NULLPTR = 161001
+MCCB_ERR_PARAM_INVALID = 161002
+MCCB_ERR_SHAPE = 561002
+MCCB_ERR_RUNTIME = -1
+
+DTYPE_CODE = {torch.bfloat16: MCCB_BF16, torch.float16: MCCB_FP16}
+
+
+# -- same names and arguments as the C-ABI -----------------------------------------------------------
+def mccb_get_workspace_size(S: int, B: int, H: int, dtype: int) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib().mccb_get_workspace_size(S, B, H, dtype, ctypes.byref(out))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_get_workspace_size")
+    return int(out.value)
+
+
+def mccb_get_plan(S: int, B: int, H: int, dtype: int) -> dict:
+    p = Plan()
+    rc = lib().mccb_get_plan(S, B, H, dtype, ctypes.byref(p))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_get_plan")
+    return {name: int(getattr(p, name)) for name, _ in Plan._fields_}
+
+
+def mccb_backward(gradY: int, x: int, weight: int, mask: int | None, gradX: int, gradWeight: int,
+                  S: int, B: int, H: int, dtype: int, workspace: int | None, workspace_size: int,
+                  stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_backward(gradY, x, weight, mask, gradX, gradWeight, S, B, H, dtype,
+                                   workspace, workspace_size, stream))
+
+
+def mccb_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def mccb_profile_begin(max_calls: int) -> None:
+    rc = lib().mccb_profile_begin(max_calls)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_profile_begin")
+
+
+def mccb_profile_end() -> tuple[float, float, int]:
+    """(summed fused-kernel ms, summed reduce-kernel ms, calls recorded)."""
+    f, r, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int(0)
+    rc = lib().mccb_profile_end(ctypes.byref(f), ctypes.byref(r), ctypes.byref(n))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_profile_end")
+    return float(f.value), float(r.value), int(n.value)
+
+
+# -- tensor front end ---------------------------------------------------------------------------------
+def _check_tensor(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must live on {device} (a HIP device)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_for(S: int, B: int, H: int, dtype: torch.dtype, device) -> torch.Tensor:
+    n = mccb_get_workspace_size(S, B, H, DTYPE_CODE[dtype])
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
+             mask: torch.Tensor | None = None, gradX: torch.Tensor | None = None,
+             gradWeight: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             stream: torch.cuda.Stream | None = None):
+    """gradX [S,B,H], gradWeight [3,H] for contiguous device tensors (outputs allocated if None).
+
+    Enqueues on `stream` (default: torch's current stream) and returns without synchronizing.
+    """
+    if gradY.dim() != 3:
+        raise ValueError("gradY must be [S,B,H]")
+    S, B, H = (int(s) for s in gradY.shape)
+    dev = gradY.device
+    dt = gradY.dtype
+    if dt not in DTYPE_CODE:
+        raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
+    _check_tensor("gradY", gradY, (S, B, H), dt, dev)
+    _check_tensor("x", x, (S, B, H), dt, dev)
+    _check_tensor("weight", weight, (3, H), dt, dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (B, S), None, dev)
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be bool or uint8")
+    if gradX is None:
+        gradX = torch.empty_like(gradY)
+    if gradWeight is None:
+        gradWeight = torch.empty_like(weight)
+    _check_tensor("gradX", gradX, (S, B, H), dt, dev)
+    _check_tensor("gradWeight", gradWeight, (3, H), dt, dev)
+    if workspace is None:
+        workspace = workspace_for(S, B, H, dt, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
+                       None if mask is None else mask.data_ptr(), gradX.data_ptr(),
+                       gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt], workspace.data_ptr(),
+                       workspace.numel(), st.cuda_stream)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_backward")
+    return gradX, gradWeight

@@ -1,0 +1,559 @@
+// mccb.hip -- masked causal depthwise conv1d backward for MI355X (gfx950).
+//
+// Computes, for gradY/x/gradX [S,B,H], weight/gradWeight [3,H] and an optional mask [B,S]
+// (page "aclnnMaskedCausalConv1dBackward", section 功能说明 / function description):
+//   gYm[i,j]     = mask[j,i] * gradY[i,j]                       (zero for i >= S)
+//   gradX[i,j]   = gYm[i,j]*w[2] + gYm[i+1,j]*w[1] + gYm[i+2,j]*w[0]
+//   gradW[k]     = sum_j sum_i gYm[i+2-k,j] * x[i,j]
+// independently for every channel h.
+//
+// Storage view: with C = B*H, the [S,B,H] tensors are an [S, C] row-major matrix; column
+// c = j*H + h never mixes with another column except that gradWeight sums the columns that share h.
+// So the whole op is a 3-tap stencil down the rows of that matrix plus a column-group reduction.
+//
+// Kernel 1 (fused): a lane owns kVec consecutive columns (one vector load) and walks a run of rows,
+// keeping the two previous masked gradY rows in registers; per row it reads one gradY row (two
+// ahead) and one x row and writes one gradX row, so HBM sees a single streaming pass. A block
+// stacks kWaves wavefronts on the same 64*kVec columns over consecutive row runs (a "strip"). The
+// strip's mask bytes are staged in LDS once. Each lane accumulates its gradWeight terms in fp64;
+// the block sums its waves in LDS in a fixed order and writes one fp64 partial per (strip, tap,
+// column) to the caller's workspace. Kernel 2 (reduce) adds the partials of each (tap, channel)
+// over strips and batches in a fixed order and rounds once. No atomics anywhere: the result bits
+// depend only on the inputs and the plan, and the plan only on (S, B, H, dtype).
+//
+// Precision: every product of two 16-bit values is exact in fp64 (and in fp32). gradX's three
+// products are summed in fp64 in the equation's order and the sum is rounded once to the dtype
+// (round-to-odd to fp32, then round-to-nearest-even, which equals direct rounding of the fp64 sum).
+// gradWeight sums stay in fp64 until the final rounding.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "mccb.h"
+
+// Tuning constants (compile-time; every value here gives the same results).
+#ifndef MCCB_VEC
+#define MCCB_VEC 4  // columns per lane: 4 -> 8-byte loads, 8 -> 16-byte loads
+#endif
+#ifndef MCCB_UNROLL
+#define MCCB_UNROLL 4  // rows whose loads a lane keeps in flight
+#endif
+#ifndef MCCB_WAVES
+#define MCCB_WAVES 4  // wavefronts per fused block, stacked along rows
+#endif
+
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;  // lanes per wavefront on CDNA
+constexpr int kVec = MCCB_VEC;
+constexpr int kWords = kVec / 2;  // 32-bit words per lane vector (two 16-bit values each)
+constexpr int kUnroll = MCCB_UNROLL;
+constexpr int kWaves = MCCB_WAVES;
+constexpr int kBlockCols = kWave * kVec;
+constexpr int kMaxBatchesPerBlock = 3;  // 512 or fewer columns span at most 3 batches if H >= 384
+constexpr int kReduceWaves = 16;        // wavefronts per reduce block
+constexpr int kReduceCols = kWave * 2;  // channels per reduce block (2 fp64 per lane)
+static_assert(kVec == 4 || kVec == 8, "lane vector must be 8 or 16 bytes");
+static_assert(kBlockCols <= 512, "mask staging assumes a block spans at most 3 batches");
+
+typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
+
+constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
+constexpr int64_t kMaxB = 32, kMaxBS = 524288;
+constexpr int64_t kMinRowsPerWave = 64, kMaxRowsPerWave = 1024;
+constexpr int64_t kTargetWaves = 16384;  // grid size (in waves) above which row runs get longer
+
+// ---------------------------------------------------------------------------------------------
+// 16-bit formats
+// ---------------------------------------------------------------------------------------------
+template <int DT>
+struct Fmt;
+
+template <>
+struct Fmt<MCCB_BF16> {
+    __device__ static inline void unpack(uint32_t u, float &lo, float &hi) {
+        lo = __uint_as_float(u << 16);
+        hi = __uint_as_float(u & 0xffff0000u);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) {  // round to nearest even
+        f32x2 f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+};
+
+template <>
+struct Fmt<MCCB_FP16> {
+    __device__ static inline void unpack(uint32_t u, float &lo, float &hi) {
+        f16x2 h = __builtin_bit_cast(f16x2, u);
+        lo = (float)h.x;
+        hi = (float)h.y;
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) {  // round to nearest even
+        f32x2 f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    }
+};
+
+// fp64 -> fp32 with round-to-odd: truncate toward zero, then force the last bit to 1 if the value
+// was inexact. Rounding the result to nearest-even in a format with at least two fewer significand
+// bits (bf16: 8, fp16: 11, against fp32's 24) gives the correctly rounded fp64 value.
+__device__ static inline float round_to_odd_f32(double d) {
+    const float f = (float)d;  // round to nearest even
+    const double back = (double)f;
+    const uint32_t b = __float_as_uint(f);
+    const uint32_t toward_zero = b - (__builtin_fabs(back) > __builtin_fabs(d) ? 1u : 0u);
+    return __uint_as_float(back != d ? (toward_zero | 1u) : b);
+}
+
+template <int DT>
+__device__ static inline void unpack_vec(const vec_t q, float (&f)[kVec]) {
+#pragma unroll
+    for (int p = 0; p < kWords; ++p) Fmt<DT>::unpack(q[p], f[2 * p], f[2 * p + 1]);
+}
+
+__device__ static inline vec_t load_vec(const vec_t *p) { return __builtin_nontemporal_load(p); }
+__device__ static inline void store_vec(vec_t *p, vec_t v) { __builtin_nontemporal_store(v, p); }
+
+// One stencil step for one lane's kVec columns at row i. In: the masked gradY rows i and i+1 in
+// fp64 (d0, d1), the raw masked row i+2 and the raw x row i. Out: the packed gradX row i. Updates
+// the gradWeight accumulators (a_k += gYm[i+2-k] * x[i]) and shifts the window by one row.
+template <int DT>
+__device__ static inline vec_t stencil_step(const vec_t gy_next, const vec_t x_row,
+                                            double (&d0)[kVec], double (&d1)[kVec],
+                                            const double (&w0)[kVec], const double (&w1)[kVec],
+                                            const double (&w2)[kVec], double (&a0)[kVec],
+                                            double (&a1)[kVec], double (&a2)[kVec]) {
+    float g2[kVec], xf[kVec];
+    unpack_vec<DT>(gy_next, g2);
+    unpack_vec<DT>(x_row, xf);
+    float out[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        const double d2 = (double)g2[e];
+        const double xd = (double)xf[e];
+        // gradX[i] = gYm[i]*w[2] + gYm[i+1]*w[1] + gYm[i+2]*w[0] (products exact in fp64)
+        double s = d0[e] * w2[e];
+        s = __builtin_fma(d1[e], w1[e], s);
+        s = __builtin_fma(d2, w0[e], s);
+        out[e] = round_to_odd_f32(s);
+        // gradWeight[k] += gYm[i+2-k] * x[i]
+        a2[e] = __builtin_fma(d0[e], xd, a2[e]);
+        a1[e] = __builtin_fma(d1[e], xd, a1[e]);
+        a0[e] = __builtin_fma(d2, xd, a0[e]);
+        d0[e] = d1[e];
+        d1[e] = d2;
+    }
+    vec_t r;
+#pragma unroll
+    for (int p = 0; p < kWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
+    return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Kernel 1: mask + gradX + gradWeight partials in one HBM pass.
+// grid.x = n_col_blocks * n_strips (column block fastest), block = kWaves * 64 lanes.
+// Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + 2) mask bytes.
+// Workspace: fp64 partials [n_strips][3][C].
+// ---------------------------------------------------------------------------------------------
+template <int DT, bool HAS_MASK>
+__global__ void __launch_bounds__(kWaves *kWave)
+    mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
+                   const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
+                   vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
+                   int64_t rows_per_wave, int64_t n_col_blocks) {
+    extern __shared__ uint8_t smask[];
+    __shared__ f64x2 red[kWaves][kBlockCols / 2];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t C = B * H;
+    const int64_t CV = C / kVec;  // lane vectors per row
+    const int64_t col_block = blockIdx.x % n_col_blocks;
+    const int64_t strip = blockIdx.x / n_col_blocks;
+    const int64_t T = rows_per_wave * kWaves;
+    const int64_t strip_row0 = strip * T;
+
+    // Lanes past the last column load a valid column (the last one) and store nothing.
+    const int64_t v_raw = col_block * kWave + lane;
+    const bool active = v_raw < CV;
+    const int64_t v = active ? v_raw : CV - 1;
+    const int64_t c = v * kVec;
+    const int64_t j = c / H;
+    const int64_t h = c - j * H;
+
+    int moff = 0;  // offset of this lane's batch in the staged mask
+    if constexpr (HAS_MASK) {
+        const int64_t c_first = col_block * kBlockCols;
+        const int64_t c_last = (c_first + kBlockCols < C ? c_first + kBlockCols : C) - 1;
+        const int64_t j_first = c_first / H;
+        const int nj = (int)(c_last / H - j_first + 1);
+        const int span = (int)(T + 2);
+        for (int t = threadIdx.x; t < nj * span; t += blockDim.x) {
+            const int jj = t / span;
+            const int64_t row = strip_row0 + (t - jj * span);
+            smask[t] = (row < S) ? mask[(j_first + jj) * S + row] : (uint8_t)0;
+        }
+        moff = (int)(j - j_first) * span;
+        __syncthreads();
+    }
+
+    double w0[kVec], w1[kVec], w2[kVec];
+    {
+        float t[kVec];
+        unpack_vec<DT>(w[(0 * H + h) / kVec], t);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) w0[e] = (double)t[e];
+        unpack_vec<DT>(w[(1 * H + h) / kVec], t);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) w1[e] = (double)t[e];
+        unpack_vec<DT>(w[(2 * H + h) / kVec], t);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) w2[e] = (double)t[e];
+    }
+
+    double a0[kVec], a1[kVec], a2[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) a0[e] = a1[e] = a2[e] = 0.0;
+
+    const int64_t r_begin = strip_row0 + wave * rows_per_wave;
+    const int64_t r_end = (r_begin + rows_per_wave < S) ? r_begin + rows_per_wave : S;
+    vec_t zero;
+#pragma unroll
+    for (int p = 0; p < kWords; ++p) zero[p] = 0u;
+
+    // Masked gradY row `row` (zero past the end).
+    auto masked_row = [&](int64_t row) -> vec_t {
+        if (row >= S) return zero;
+        vec_t q = load_vec(gy + row * CV + v);
+        if constexpr (HAS_MASK) {
+            if (smask[moff + (int)(row - strip_row0)] == 0) q = zero;
+        }
+        return q;
+    };
+
+    if (r_begin < r_end) {
+        double d0[kVec], d1[kVec];
+        {
+            float f0[kVec], f1[kVec];
+            unpack_vec<DT>(masked_row(r_begin), f0);
+            unpack_vec<DT>(masked_row(r_begin + 1), f1);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                d0[e] = (double)f0[e];
+                d1[e] = (double)f1[e];
+            }
+        }
+
+        int64_t i = r_begin;
+        const vec_t *py = gy + (i + 2) * CV + v;
+        const vec_t *px = x + i * CV + v;
+        vec_t *pg = gx + i * CV + v;
+        // Steady state: rows i .. i+kUnroll-1 and their look-ahead rows all lie inside [0, S).
+        for (; i + kUnroll <= r_end && i + kUnroll + 2 <= S; i += kUnroll) {
+            vec_t qy[kUnroll], qx[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                qy[u] = load_vec(py + u * CV);
+                qx[u] = load_vec(px + u * CV);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                vec_t q = qy[u];
+                if constexpr (HAS_MASK) {
+                    if (smask[moff + (int)(i + 2 + u - strip_row0)] == 0) q = zero;
+                }
+                const vec_t r = stencil_step<DT>(q, qx[u], d0, d1, w0, w1, w2, a0, a1, a2);
+                if (active) store_vec(pg + u * CV, r);
+            }
+            py += kUnroll * CV;
+            px += kUnroll * CV;
+            pg += kUnroll * CV;
+        }
+        // Tail: one row at a time; look-ahead rows past S read as zero.
+        for (; i < r_end; ++i) {
+            const vec_t q = masked_row(i + 2);
+            const vec_t r =
+                stencil_step<DT>(q, load_vec(x + i * CV + v), d0, d1, w0, w1, w2, a0, a1, a2);
+            if (active) store_vec(gx + i * CV + v, r);
+        }
+    }
+
+    // gradWeight partials of the strip: add the kWaves waves in a fixed order (wave 0 first).
+    const int64_t col0 = col_block * kBlockCols;
+    for (int k = 0; k < 3; ++k) {
+        const double *acc = (k == 0) ? a0 : (k == 1) ? a1 : a2;
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kVec / 2; ++p) red[wave][lane * (kVec / 2) + p] = f64x2{acc[2 * p], acc[2 * p + 1]};
+        __syncthreads();
+        const double *flat = reinterpret_cast<const double *>(&red[0][0]);
+        for (int t = threadIdx.x; t < kBlockCols; t += blockDim.x) {
+            double s = flat[t];
+#pragma unroll
+            for (int q = 1; q < kWaves; ++q) s += flat[q * kBlockCols + t];
+            const int64_t col = col0 + t;
+            if (col < C) ws[(strip * 3 + k) * C + col] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Kernel 2: gradWeight[k,h] = sum over strips s (outer) and batches j (inner) of
+// ws[s][k][j*H + h], in fp64, then one rounding to the dtype.
+// grid = (ceil(H / 128), 3), block = kReduceWaves * 64 lanes; a lane owns 2 channels. Each wave
+// sums a contiguous range of the (s, j) rows; the waves' sums are then added in wave order.
+// ---------------------------------------------------------------------------------------------
+template <int DT>
+__global__ void __launch_bounds__(kReduceWaves *kWave)
+    mccb_gw_reduce(const double *__restrict__ ws, uint32_t *__restrict__ gw, int64_t n_strips,
+                   int64_t B, int64_t H) {
+    __shared__ f64x2 red[kReduceWaves][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int k = blockIdx.y;
+    const int64_t h = (int64_t)blockIdx.x * kReduceCols + lane * 2;
+    const int64_t C = B * H;
+    const int64_t rows = n_strips * B;
+    const int64_t per = (rows + kReduceWaves - 1) / kReduceWaves;
+    const int64_t lo = wave * per;
+    const int64_t hi = (lo + per < rows) ? lo + per : rows;
+
+    f64x2 acc = {0.0, 0.0};
+    if (h < H && lo < hi) {
+        int64_t s = lo / B, jj = lo - (lo / B) * B;
+#pragma unroll 4
+        for (int64_t r = lo; r < hi; ++r) {
+            acc += *reinterpret_cast<const f64x2 *>(ws + (s * 3 + k) * C + jj * H + h);
+            if (++jj == B) {
+                jj = 0;
+                ++s;
+            }
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && h < H) {
+        f64x2 t = red[0][lane];
+        for (int q = 1; q < kReduceWaves; ++q) t += red[q][lane];
+        // gradWeight[k, h .. h+1]: one 32-bit word at element offset k*H + h (h even).
+        gw[(k * H + h) / 2] = Fmt<DT>::pack(round_to_odd_f32(t[0]), round_to_odd_f32(t[1]));
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side: validation, plan, launch.
+// ---------------------------------------------------------------------------------------------
+struct Plan {
+    int64_t S, B, H, C;
+    int dtype;
+    int64_t rows_per_wave, rows_per_strip, n_strips, n_col_blocks;
+    uint64_t ws_bytes;
+};
+
+int check_shape(int64_t S, int64_t B, int64_t H, int dtype) {
+    if (dtype != MCCB_BF16 && dtype != MCCB_FP16) return MCCB_ERR_PARAM_INVALID;
+    if (B < 1 || B > kMaxB || S < 1 || S > kMaxBS || B * S > kMaxBS) return MCCB_ERR_SHAPE;
+    if (H < kMinH || H > kMaxH || H % kHAlign != 0) return MCCB_ERR_SHAPE;
+    return MCCB_OK;
+}
+
+// Pure function of (S, B, H, dtype) -- never of the device -- so gradWeight's summation order, and
+// therefore its bits, are the same on every run and every MI355X.
+Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype) {
+    Plan p;
+    p.S = S;
+    p.B = B;
+    p.H = H;
+    p.C = B * H;
+    p.dtype = dtype;
+    p.n_col_blocks = (p.C + kBlockCols - 1) / kBlockCols;
+    // Start at kMinRowsPerWave rows per wave and double while the grid keeps at least
+    // kTargetWaves waves: longer row runs cut the partial traffic (16 bytes per column per strip
+    // written and read back, against 6 bytes per element streamed) and the 2-row look-ahead
+    // re-read at the end of every run.
+    auto waves_for = [&](int64_t rpw) {
+        const int64_t strips = (S + rpw * kWaves - 1) / (rpw * kWaves);
+        return strips * p.n_col_blocks * kWaves;
+    };
+    int64_t r = kMinRowsPerWave;
+    while (r < kMaxRowsPerWave && waves_for(2 * r) >= kTargetWaves) r *= 2;
+    p.rows_per_wave = r;
+    p.rows_per_strip = r * kWaves;
+    p.n_strips = (S + p.rows_per_strip - 1) / p.rows_per_strip;
+    p.ws_bytes = (uint64_t)p.n_strips * 3u * (uint64_t)p.C * sizeof(double);
+    return p;
+}
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Optional event-based timing of the two kernels.
+struct Profile {
+    std::mutex mu;
+    bool on = false;
+    int cap = 0, n = 0;
+    std::vector<hipEvent_t> ev;  // 3 per call: before kernel 1, between, after kernel 2
+} g_prof;
+
+template <int DT>
+hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, const uint8_t *mask,
+                  void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev) {
+    const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
+    const dim3 block1(kWaves * kWave);
+    if (ev) hipEventRecord(ev[0], st);
+    if (mask) {
+        const size_t lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + 2);
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1, lds, st, (const vec_t *)gy,
+                           (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx, (double *)ws,
+                           p.S, p.B, p.H, p.rows_per_wave, p.n_col_blocks);
+    } else {
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, false>), grid1, block1, 0, st, (const vec_t *)gy,
+                           (const vec_t *)x, (const vec_t *)w, (const uint8_t *)nullptr,
+                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_wave,
+                           p.n_col_blocks);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev) hipEventRecord(ev[1], st);
+    const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), 3);
+    const dim3 block2(kReduceWaves * kWave);
+    hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
+                       (uint32_t *)gw, p.n_strips, p.B, p.H);
+    e = hipGetLastError();
+    if (ev) hipEventRecord(ev[2], st);
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mccb_get_workspace_size(int64_t S, int64_t B, int64_t H, int dtype, uint64_t *workspace_size) {
+    if (!workspace_size) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    *workspace_size = make_plan(S, B, H, dtype).ws_bytes;
+    return MCCB_OK;
+}
+
+int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan) {
+    if (!plan) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(S, B, H, dtype);
+    plan->rows_per_wave = p.rows_per_wave;
+    plan->rows_per_strip = p.rows_per_strip;
+    plan->n_strips = p.n_strips;
+    plan->cols_per_block = kBlockCols;
+    plan->n_col_blocks = p.n_col_blocks;
+    plan->waves_per_block = kWaves;
+    plan->workspace_size = p.ws_bytes;
+    return MCCB_OK;
+}
+
+int mccb_backward(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                  void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
+                  void *workspace, uint64_t workspace_size, void *stream) {
+    if (!gradY || !x || !weight || !gradX || !gradWeight) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(S, B, H, dtype);
+    if (p.ws_bytes > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
+    if (workspace_size < p.ws_bytes) return MCCB_ERR_PARAM_INVALID;
+    if (!aligned16(gradY) || !aligned16(x) || !aligned16(weight) || !aligned16(gradX) ||
+        !aligned16(gradWeight) || (p.ws_bytes > 0 && !aligned16(workspace)))
+        return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
+    const uint64_t mb = mask ? (uint64_t)(B * S) : 0u;
+    // No output (nor the workspace) may overlap any other buffer; in particular gradX cannot
+    // alias gradY, whose rows the stencil reads ahead of the rows it writes.
+    const void *bufs[7] = {gradY, x, weight, mask, gradX, gradWeight, workspace};
+    const uint64_t lens[7] = {nb, nb, wb, mb, nb, wb, p.ws_bytes};
+    for (int o = 4; o < 7; ++o) {
+        if (!bufs[o] || lens[o] == 0) continue;
+        for (int t = 0; t < 7; ++t) {
+            if (t == o || !bufs[t] || lens[t] == 0) continue;
+            if (overlaps(bufs[o], lens[o], bufs[t], lens[t])) return MCCB_ERR_PARAM_INVALID;
+        }
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t *ev = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.on && g_prof.n < g_prof.cap) ev = &g_prof.ev[3 * (size_t)g_prof.n++];
+    }
+    const hipError_t e =
+        (dtype == MCCB_BF16)
+            ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev)
+            : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+const char *mccb_status_string(int status) {
+    switch (status) {
+        case MCCB_OK: return "MCCB_OK";
+        case MCCB_ERR_PARAM_NULLPTR: return "MCCB_ERR_PARAM_NULLPTR: a required pointer is NULL";
+        case MCCB_ERR_PARAM_INVALID:
+            return "MCCB_ERR_PARAM_INVALID: bad dtype, alignment, overlap or workspace size";
+        case MCCB_ERR_SHAPE: return "MCCB_ERR_SHAPE: shape outside the supported range";
+        case MCCB_ERR_RUNTIME: return "MCCB_ERR_RUNTIME: HIP launch failed";
+        default: return "unknown mccb status";
+    }
+}
+
+int mccb_profile_begin(int max_calls) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (hipEvent_t e : g_prof.ev)
+        if (e) hipEventDestroy(e);
+    g_prof.on = false;
+    g_prof.cap = g_prof.n = 0;
+    g_prof.ev.assign(3 * (size_t)(max_calls > 0 ? max_calls : 0), nullptr);
+    for (hipEvent_t &e : g_prof.ev)
+        if (hipEventCreate(&e) != hipSuccess) return MCCB_ERR_RUNTIME;
+    g_prof.cap = max_calls > 0 ? max_calls : 0;
+    g_prof.on = true;
+    return MCCB_OK;
+}
+
+int mccb_profile_end(double *fused_ms, double *reduce_ms, int *calls) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    double f = 0.0, r = 0.0;
+    int rc = MCCB_OK;
+    for (int c = 0; c < g_prof.n; ++c) {
+        hipEvent_t *e = &g_prof.ev[3 * (size_t)c];
+        float a = 0.f, b = 0.f;
+        if (hipEventSynchronize(e[2]) != hipSuccess ||
+            hipEventElapsedTime(&a, e[0], e[1]) != hipSuccess ||
+            hipEventElapsedTime(&b, e[1], e[2]) != hipSuccess) {
+            rc = MCCB_ERR_RUNTIME;
+            break;
+        }
+        f += a;
+        r += b;
+    }
+    if (fused_ms) *fused_ms = f;
+    if (reduce_ms) *reduce_ms = r;
+    if (calls) *calls = g_prof.n;
+    for (hipEvent_t e : g_prof.ev)
+        if (e) hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.on = false;
+    g_prof.cap = g_prof.n = 0;
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/mccb.h
+declares, validates arguments on the host (before any HIP call) with the error classes of the page's
+return-code table, and plans tiles as a pure function of the shape.
+
+Every call below that passes made-up pointer values is one that validation must reject; a call that
+got past validation would reach a kernel launch, so each such call asserts a validation code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import masked_depthwise_causal_amd as mdc
+from masked_depthwise_causal_amd import build as mbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mccb.h")
+
+BF16, FP16 = mdc.MCCB_BF16, mdc.MCCB_FP16
+OK, NULLPTR, INVALID, SHAPE = mdc.MCCB_OK, mdc.MCCB_ERR_PARAM_NULLPTR, mdc.MCCB_ERR_PARAM_INVALID, \
+    mdc.MCCB_ERR_SHAPE
+VALIDATION_CODES = {NULLPTR, INVALID, SHAPE}
+
+# Made-up, widely separated, 256-byte aligned "device addresses" (never dereferenced).
+GB = 1 << 30
+GY, X, W, M, GX, GW, WS = (0x7F0000000000 + k * 64 * GB for k in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mccb_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mccb_get_workspace_size", "mccb_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mdc.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mbuild.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mccb_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def _ws(S, B, H, dt=BF16):
+    return mdc.mccb_get_workspace_size(S, B, H, dt)
+
+
+def call(gy=GY, x=X, w=W, m=M, gx=GX, gw=GW, S=64, B=2, H=384, dt=BF16, ws=WS, wsz=None,
+         stream=None):
+    if wsz is None:
+        wsz = _ws(S, B, H, dt) if dt in (BF16, FP16) else 0
+    rc = mdc.mccb_backward(gy, x, w, m, gx, gw, S, B, H, dt, ws, wsz, stream)
+    assert rc in VALIDATION_CODES, f"call passed validation with fake pointers (rc={rc})"
+    return rc
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
+def test_null_required_pointer(which):
+    assert call(**{which: None}) == NULLPTR
+
+
+def test_null_workspace_when_required():
+    assert call(ws=None) == NULLPTR
+
+
+def test_null_size_out_pointer():
+    rc = mdc.lib().mccb_get_workspace_size(64, 2, 384, BF16, None)
+    assert rc == NULLPTR
+    assert mdc.lib().mccb_get_plan(64, 2, 384, BF16, None) == NULLPTR
+
+
+@pytest.mark.parametrize("dt", [-1, 2, 7])
+def test_bad_dtype(dt):
+    assert call(dt=dt, wsz=1 << 40) == INVALID
+    out = ctypes.c_uint64(0)
+    assert mdc.lib().mccb_get_workspace_size(64, 2, 384, dt, ctypes.byref(out)) == INVALID
+
+
+@pytest.mark.parametrize("S,B,H", [
+    (64, 0, 384), (64, 33, 384), (0, 2, 384), (-5, 2, 384), (524288, 2, 384), (16385, 32, 384),
+    (64, 2, 320), (64, 2, 24640), (64, 2, 400), (64, 2, 448 + 32), (1, 1, 0), (2 ** 40, 1, 384)])
+def test_shape_out_of_range(S, B, H):
+    out = ctypes.c_uint64(0)
+    assert mdc.lib().mccb_get_workspace_size(S, B, H, BF16, ctypes.byref(out)) == SHAPE
+    assert call(S=S, B=B, H=H, wsz=1 << 40) == SHAPE
+
+
+@pytest.mark.parametrize("S,B,H", [(1, 1, 384), (524288, 1, 384), (16384, 32, 5120),
+                                   (262144, 2, 24576), (1, 32, 24576), (3, 7, 448)])
+def test_shape_limits_accepted(S, B, H):
+    # the limits themselves are valid (constraints section: B 1..32, B*S 1..512K, H 384..24576)
+    assert _ws(S, B, H) > 0
+
+
+def test_workspace_too_small():
+    need = _ws(64, 2, 384)
+    assert call(wsz=need - 1) == INVALID
+    assert call(wsz=0) == INVALID
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw", "ws"])
+def test_misaligned_pointer(which):
+    base = {"gy": GY, "x": X, "w": W, "gx": GX, "gw": GW, "ws": WS}[which]
+    assert call(**{which: base + 8}) == INVALID
+
+
+@pytest.mark.parametrize("case", [
+    dict(gx=GY), dict(gx=X + 1024), dict(gx=W), dict(gw=GX + 256), dict(gw=X), dict(gw=W),
+    dict(ws=GY + 4096), dict(ws=GX), dict(ws=GW), dict(gx=M - 512)])
+def test_overlapping_buffers(case):
+    assert call(**case) == INVALID
+
+
+def test_plan_is_pure_and_consistent():
+    for (S, B, H, dt) in [(64, 1, 384, BF16), (4096, 4, 4096, BF16), (8192, 8, 8192, FP16),
+                          (16384, 32, 5120, BF16), (262144, 2, 24576, BF16), (1, 1, 384, FP16),
+                          (1000, 3, 448, BF16)]:
+        p1 = mdc.mccb_get_plan(S, B, H, dt)
+        p2 = mdc.mccb_get_plan(S, B, H, dt)
+        assert p1 == p2
+        C = B * H
+        assert p1["rows_per_strip"] == p1["rows_per_wave"] * p1["waves_per_block"]
+        assert p1["n_strips"] == -(-S // p1["rows_per_strip"])
+        assert p1["n_col_blocks"] == -(-C // p1["cols_per_block"])
+        assert p1["workspace_size"] == p1["n_strips"] * 3 * C * 8
+        assert p1["workspace_size"] == _ws(S, B, H, dt)
+        # the plan does not depend on the dtype
+        other = FP16 if dt == BF16 else BF16
+        assert mdc.mccb_get_plan(S, B, H, other) == p1
+
+
+def test_workspace_stays_small_at_the_headline_shape():
+    # fp64 partials: bounded well below 1 % of the 16.1 GB streamed at S=16384, B=32, H=5120
+    assert _ws(16384, 32, 5120) < 0.005 * 3 * 16384 * 32 * 5120 * 2
+
+
+def test_status_strings():
+    for code in (OK, NULLPTR, INVALID, SHAPE, mdc.MCCB_ERR_RUNTIME, 12345):
+        s = mdc.mccb_status_string(code)
+        assert isinstance(s, str) and s
+    assert "NULLPTR" in mdc.mccb_status_string(NULLPTR)
+    assert "SHAPE" in mdc.mccb_status_string(SHAPE)
+
+
+def test_python_binding_raises_on_bad_shape():
+    with pytest.raises(mdc.MccbError) as e:
+        mdc.mccb_get_workspace_size(64, 2, 100, BF16)
+    assert e.value.status == SHAPE

@@ -1,0 +1,131 @@
+"""GPU parity: the HIP path against the CPU fp64 oracle on the same seeded inputs.
+
+Bars (stated in the tests): gradX within 1 ulp of the oracle's correctly rounded value (and, by
+design, bit-exact); gradWeight within relative error 8e-3 (bf16) / 1e-3 (fp16) of the oracle's exact
+fp64 value (and, by design, equal to its rounding up to 1 ulp). Small shapes are compared element by
+element; the full-size workloads, in the launch configuration the benchmark times, are compared on
+every element of sampled channels and of sampled rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import masked_depthwise_causal_amd as mdc
+from synth import WORKLOADS, custom
+from synth import workloads as wls
+
+from .gpu_util import (announce, bits16, compare_columns, compare_full, compare_rows, gpu_inputs,
+                       gpu_run, sample_channels, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def plan_of(wl):
+    return mdc.mccb_get_plan(wl.S, wl.B, wl.H, mdc.MCCB_BF16 if wl.dtype == "bf16" else mdc.MCCB_FP16)
+
+
+def test_small_workload_full():
+    wl = WORKLOADS[0]  # S=64 B=1 H=384 bf16, Bernoulli(0.8) mask
+    gx, gw = gpu_run(wl)
+    compare_full(wl, gx, gw)
+
+
+def test_call_example_all_zero():
+    # the page's call example: S=1, B=2, H=384, FLOAT16, every input and the mask zero
+    S, B, H = 1, 2, 384
+    z = torch.zeros((S, B, H), dtype=torch.float16, device="cuda")
+    w = torch.zeros((3, H), dtype=torch.float16, device="cuda")
+    m = torch.zeros((B, S), dtype=torch.uint8, device="cuda")
+    gx = torch.full_like(z, 7.0)
+    gw = torch.full_like(w, 7.0)
+    announce("call example S=1 B=2 H=384 fp16 zeros")
+    mdc.backward(z, z.clone(), w, m, gradX=gx, gradWeight=gw)
+    torch.cuda.synchronize()
+    assert torch.all(gx == 0) and torch.all(gw == 0)
+
+
+EDGE = [
+    # (S, B, H, dtype, mask)
+    (1, 2, 384, "bf16", ("bernoulli", 0.8)),
+    (2, 2, 384, "bf16", ("null",)),
+    (3, 3, 384, "fp16", ("bernoulli", 0.5)),
+    (4, 1, 384, "bf16", ("all_true",)),
+    (5, 2, 448, "fp16", ("prefix",)),
+    (63, 1, 384, "bf16", ("bernoulli", 0.9)),
+    (64, 1, 384, "bf16", ("bernoulli", 0.9)),
+    (65, 1, 384, "bf16", ("bernoulli", 0.9)),
+    (66, 3, 640, "bf16", ("bernoulli", 0.7)),
+    (255, 2, 384, "fp16", ("null",)),
+    (256, 2, 384, "bf16", ("bernoulli", 0.6)),
+    (257, 2, 448, "bf16", ("prefix",)),
+    (258, 5, 384, "fp16", ("bernoulli", 0.9)),
+    (513, 3, 576, "bf16", ("null",)),
+    (1000, 7, 448, "bf16", ("bernoulli", 0.8)),
+    (16, 32, 384, "bf16", ("bernoulli", 0.5)),
+    (16, 32, 384, "fp16", ("all_false",)),
+    (8, 1, 24576, "bf16", ("bernoulli", 0.9)),
+    (3, 2, 24576, "fp16", ("null",)),
+]
+
+
+@pytest.mark.parametrize("S,B,H,dtype,mask", EDGE, ids=lambda v: str(v))
+def test_edge_shapes_full(S, B, H, dtype, mask):
+    if mask[0] == "all_false":
+        wl = custom(S, B, H, dtype, ("bernoulli", 0.0), seed=S * 31 + B)
+    else:
+        wl = custom(S, B, H, dtype, mask, seed=S * 31 + B)
+    gx, gw = gpu_run(wl, poison_workspace=True)
+    compare_full(wl, gx, gw)
+
+
+def test_tile_boundaries_full():
+    """S on and around the strip and wave-run boundaries the plan picks for this shape."""
+    B, H = 2, 384
+    base = mdc.mccb_get_plan(4096, B, H, mdc.MCCB_BF16)
+    R, T = base["rows_per_wave"], base["rows_per_strip"]
+    for S in sorted({R - 1, R + 1, R + 2, T - 1, T, T + 1, T + 2, 2 * T + 3}):
+        wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S)
+        gx, gw = gpu_run(wl)
+        compare_full(wl, gx, gw, tag=f"S={S} (R={R}, T={T})")
+
+
+def test_subnormal_outputs_full():
+    # results in the subnormal range of each format must still be correctly rounded
+    cases = [custom(70, 2, 384, "fp16", ("bernoulli", 0.8), seed=5, gy=("normal", 2e-3),
+                    x=("normal", 1e-3), w=("normal", 1e-2)),
+             custom(70, 2, 384, "bf16", ("bernoulli", 0.8), seed=6, gy=("normal", 2.0 ** -118),
+                    x=("normal", 2.0 ** -10), w=("normal", 2.0 ** -12))]
+    for wl in cases:
+        gx, gw = gpu_run(wl)
+        compare_full(wl, gx, gw, tag=wl.name + " subnormal")
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=lambda i: WORKLOADS[i].name)
+def test_full_size_workload_sampled(idx):
+    wl = WORKLOADS[idx]
+    inputs = gpu_inputs(wl)
+    gx, gw = gpu_run(wl, inputs)
+    announce(f"compare {wl.name}: sampled channels")
+    compare_columns(wl, gx, gw, sample_channels(wl, seed=idx))
+    announce(f"compare {wl.name}: sampled rows")
+    compare_rows(wl, gx, sample_rows(wl, plan_of(wl), seed=idx))
+    # a second run on the same inputs gives the same bits
+    gx2, gw2 = gpu_run(wl, inputs, poison_workspace=True)
+    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16))
+    assert torch.equal(gw.view(torch.int16), gw2.view(torch.int16))
+    del gx, gw, gx2, gw2, inputs
+    torch.cuda.empty_cache()
+
+
+def test_generator_same_bits_on_gpu_and_cpu():
+    """The oracle regenerates its inputs on the CPU: check the GPU-generated tensors agree."""
+    wl = WORKLOADS[3]
+    small = custom(64, 4, 512, "bf16", ("bernoulli", 0.9), seed=wl.seed)
+    g_gpu = wls.full_tensor(small, wls.STREAM_GY, "cuda").cpu()
+    g_cpu = wls.full_tensor(small, wls.STREAM_GY, "cpu")
+    assert torch.equal(g_gpu.view(torch.int16), g_cpu.view(torch.int16))
+    hs = torch.tensor([0, 5, 511])
+    assert torch.equal(wls.column_tensor(small, wls.STREAM_GY, hs).view(torch.int16),
+                       g_cpu[:, :, hs].contiguous().view(torch.int16))
