@@ -45,6 +45,15 @@
 #ifndef MCCB_WAVES
 #define MCCB_WAVES 4  // wavefronts per fused block, stacked along rows
 #endif
+#ifndef MCCB_NT_LOAD
+#define MCCB_NT_LOAD 1  // streaming (non-temporal) hint on gradY / x loads
+#endif
+#ifndef MCCB_NT_STORE
+#define MCCB_NT_STORE 1  // streaming (non-temporal) hint on gradX stores
+#endif
+#ifndef MCCB_TARGET_WAVES
+#define MCCB_TARGET_WAVES 16384  // grid size (in waves) above which row runs get longer
+#endif
 
 namespace {
 
@@ -70,7 +79,7 @@ typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
 constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
 constexpr int64_t kMinRowsPerWave = 64, kMaxRowsPerWave = 1024;
-constexpr int64_t kTargetWaves = 16384;  // grid size (in waves) above which row runs get longer
+constexpr int64_t kTargetWaves = MCCB_TARGET_WAVES;
 
 // ---------------------------------------------------------------------------------------------
 // 16-bit formats
@@ -120,42 +129,57 @@ __device__ static inline void unpack_vec(const vec_t q, float (&f)[kVec]) {
     for (int p = 0; p < kWords; ++p) Fmt<DT>::unpack(q[p], f[2 * p], f[2 * p + 1]);
 }
 
-__device__ static inline vec_t load_vec(const vec_t *p) { return __builtin_nontemporal_load(p); }
-__device__ static inline void store_vec(vec_t *p, vec_t v) { __builtin_nontemporal_store(v, p); }
+__device__ static inline vec_t load_vec(const vec_t *p) {
+#if MCCB_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ static inline void store_vec(vec_t *p, vec_t v) {
+#if MCCB_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
 
-// One stencil step for one lane's kVec columns at row i. In: the masked gradY rows i and i+1 in
-// fp64 (d0, d1), the raw masked row i+2 and the raw x row i. Out: the packed gradX row i. Updates
-// the gradWeight accumulators (a_k += gYm[i+2-k] * x[i]) and shifts the window by one row.
+// gradX for one lane's kVec columns at row i from the masked gradY rows i, i+1, i+2 (fp64), and
+// the gradWeight terms of row i: a_k += gYm[i+2-k] * x[i]. Returns the packed gradX row.
 template <int DT>
-__device__ static inline vec_t stencil_step(const vec_t gy_next, const vec_t x_row,
-                                            double (&d0)[kVec], double (&d1)[kVec],
-                                            const double (&w0)[kVec], const double (&w1)[kVec],
-                                            const double (&w2)[kVec], double (&a0)[kVec],
-                                            double (&a1)[kVec], double (&a2)[kVec]) {
-    float g2[kVec], xf[kVec];
-    unpack_vec<DT>(gy_next, g2);
+__device__ static inline vec_t stencil_row(const double (&d0)[kVec], const double (&d1)[kVec],
+                                           const double (&d2)[kVec], const vec_t x_row,
+                                           const double (&w0)[kVec], const double (&w1)[kVec],
+                                           const double (&w2)[kVec], double (&a0)[kVec],
+                                           double (&a1)[kVec], double (&a2)[kVec]) {
+    float xf[kVec];
     unpack_vec<DT>(x_row, xf);
     float out[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        const double d2 = (double)g2[e];
-        const double xd = (double)xf[e];
         // gradX[i] = gYm[i]*w[2] + gYm[i+1]*w[1] + gYm[i+2]*w[0] (products exact in fp64)
         double s = d0[e] * w2[e];
         s = __builtin_fma(d1[e], w1[e], s);
-        s = __builtin_fma(d2, w0[e], s);
+        s = __builtin_fma(d2[e], w0[e], s);
         out[e] = round_to_odd_f32(s);
         // gradWeight[k] += gYm[i+2-k] * x[i]
+        const double xd = (double)xf[e];
         a2[e] = __builtin_fma(d0[e], xd, a2[e]);
         a1[e] = __builtin_fma(d1[e], xd, a1[e]);
-        a0[e] = __builtin_fma(d2, xd, a0[e]);
-        d0[e] = d1[e];
-        d1[e] = d2;
+        a0[e] = __builtin_fma(d2[e], xd, a0[e]);
     }
     vec_t r;
 #pragma unroll
     for (int p = 0; p < kWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
     return r;
+}
+
+template <int DT>
+__device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
+    float f[kVec];
+    unpack_vec<DT>(q, f);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) d[e] = (double)f[e];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -174,7 +198,9 @@ __global__ void __launch_bounds__(kWaves *kWave)
     __shared__ f64x2 red[kWaves][kBlockCols / 2];
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // The wave index is the same on every lane of a wave; saying so keeps everything derived from
+    // it (row ranges, row addresses) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t C = B * H;
     const int64_t CV = C / kVec;  // lane vectors per row
     const int64_t col_block = blockIdx.x % n_col_blocks;
@@ -241,29 +267,27 @@ __global__ void __launch_bounds__(kWaves *kWave)
     };
 
     if (r_begin < r_end) {
-        double d0[kVec], d1[kVec];
-        {
-            float f0[kVec], f1[kVec];
-            unpack_vec<DT>(masked_row(r_begin), f0);
-            unpack_vec<DT>(masked_row(r_begin + 1), f1);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                d0[e] = (double)f0[e];
-                d1[e] = (double)f1[e];
-            }
-        }
+        // dw[0], dw[1]: masked gradY rows i, i+1 in fp64, carried across iterations.
+        double dw[kUnroll + 2][kVec];
+        widen<DT>(masked_row(r_begin), dw[0]);
+        widen<DT>(masked_row(r_begin + 1), dw[1]);
+
+        // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
+        // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
+        const int64_t row_bytes = C * 2;
+        const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
+        const char *gy_rows = reinterpret_cast<const char *>(gy) + (r_begin + 2) * row_bytes;
+        const char *x_rows = reinterpret_cast<const char *>(x) + r_begin * row_bytes;
+        char *gx_rows = reinterpret_cast<char *>(gx) + r_begin * row_bytes;
 
         int64_t i = r_begin;
-        const vec_t *py = gy + (i + 2) * CV + v;
-        const vec_t *px = x + i * CV + v;
-        vec_t *pg = gx + i * CV + v;
         // Steady state: rows i .. i+kUnroll-1 and their look-ahead rows all lie inside [0, S).
         for (; i + kUnroll <= r_end && i + kUnroll + 2 <= S; i += kUnroll) {
             vec_t qy[kUnroll], qx[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                qy[u] = load_vec(py + u * CV);
-                qx[u] = load_vec(px + u * CV);
+                qy[u] = load_vec(reinterpret_cast<const vec_t *>(gy_rows + u * row_bytes + lane_off));
+                qx[u] = load_vec(reinterpret_cast<const vec_t *>(x_rows + u * row_bytes + lane_off));
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -271,19 +295,34 @@ __global__ void __launch_bounds__(kWaves *kWave)
                 if constexpr (HAS_MASK) {
                     if (smask[moff + (int)(i + 2 + u - strip_row0)] == 0) q = zero;
                 }
-                const vec_t r = stencil_step<DT>(q, qx[u], d0, d1, w0, w1, w2, a0, a1, a2);
-                if (active) store_vec(pg + u * CV, r);
+                widen<DT>(q, dw[u + 2]);
             }
-            py += kUnroll * CV;
-            px += kUnroll * CV;
-            pg += kUnroll * CV;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const vec_t r =
+                    stencil_row<DT>(dw[u], dw[u + 1], dw[u + 2], qx[u], w0, w1, w2, a0, a1, a2);
+                if (active) store_vec(reinterpret_cast<vec_t *>(gx_rows + u * row_bytes + lane_off), r);
+            }
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                dw[0][e] = dw[kUnroll][e];
+                dw[1][e] = dw[kUnroll + 1][e];
+            }
+            gy_rows += kUnroll * row_bytes;
+            x_rows += kUnroll * row_bytes;
+            gx_rows += kUnroll * row_bytes;
         }
         // Tail: one row at a time; look-ahead rows past S read as zero.
         for (; i < r_end; ++i) {
-            const vec_t q = masked_row(i + 2);
-            const vec_t r =
-                stencil_step<DT>(q, load_vec(x + i * CV + v), d0, d1, w0, w1, w2, a0, a1, a2);
+            widen<DT>(masked_row(i + 2), dw[2]);
+            const vec_t r = stencil_row<DT>(dw[0], dw[1], dw[2], load_vec(x + i * CV + v), w0, w1,
+                                            w2, a0, a1, a2);
             if (active) store_vec(gx + i * CV + v, r);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                dw[0][e] = dw[1][e];
+                dw[1][e] = dw[2][e];
+            }
         }
     }
 
@@ -413,7 +452,7 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
                   void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev) {
     const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
     const dim3 block1(kWaves * kWave);
-    if (ev) hipEventRecord(ev[0], st);
+    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
     if (mask) {
         const size_t lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + 2);
         hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1, lds, st, (const vec_t *)gy,
@@ -427,13 +466,13 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev) hipEventRecord(ev[1], st);
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hipErrorInvalidValue;
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), 3);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
                        (uint32_t *)gw, p.n_strips, p.B, p.H);
     e = hipGetLastError();
-    if (ev) hipEventRecord(ev[2], st);
+    if (e == hipSuccess && ev && hipEventRecord(ev[2], st) != hipSuccess) return hipErrorInvalidValue;
     return e;
 }
 
@@ -518,7 +557,7 @@ const char *mccb_status_string(int status) {
 int mccb_profile_begin(int max_calls) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     for (hipEvent_t e : g_prof.ev)
-        if (e) hipEventDestroy(e);
+        if (e) (void)hipEventDestroy(e);
     g_prof.on = false;
     g_prof.cap = g_prof.n = 0;
     g_prof.ev.assign(3 * (size_t)(max_calls > 0 ? max_calls : 0), nullptr);
@@ -549,7 +588,7 @@ int mccb_profile_end(double *fused_ms, double *reduce_ms, int *calls) {
     if (reduce_ms) *reduce_ms = r;
     if (calls) *calls = g_prof.n;
     for (hipEvent_t e : g_prof.ev)
-        if (e) hipEventDestroy(e);
+        if (e) (void)hipEventDestroy(e);
     g_prof.ev.clear();
     g_prof.on = false;
     g_prof.cap = g_prof.n = 0;

@@ -13,6 +13,10 @@ import oracle
 from synth import workloads as wls
 
 RTOL = {"bf16": 8e-3, "fp16": 1e-3}  # gradWeight relative-error bar per dtype
+# Spacing of the subnormal range of each dtype. A relative bar cannot hold for results below the
+# smallest normal number (even the correctly rounded value misses it), so there the bound is one
+# subnormal step.
+SUBNORMAL_STEP = {"bf16": 2.0 ** -133, "fp16": 2.0 ** -24}
 
 
 def announce(msg: str) -> None:
@@ -67,7 +71,7 @@ def check_gradw(gpu_bits: np.ndarray, ref: dict, dtype: str, tag: str, cols=None
     gw64 = ref["gw64"] if cols is None else ref["gw64"][:, cols]
     got = oracle.get().decode(dtype, gpu_bits)  # decoding is exact, see the oracle's pins
     err = np.abs(got - gw64)
-    bound = RTOL[dtype] * np.abs(gw64)
+    bound = np.maximum(RTOL[dtype] * np.abs(gw64), SUBNORMAL_STEP[dtype])
     bad = err > bound
     assert not bad.any(), (f"{tag}: gradWeight rel err > {RTOL[dtype]} at {np.argwhere(bad)[:5]}, "
                            f"max rel {float((err / np.maximum(np.abs(gw64), 1e-300)).max())}")
