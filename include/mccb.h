@@ -27,8 +27,8 @@
  * All five floating-point tensors share one dtype, bfloat16 or float16 (parameter table).
  *
  * Results: gradX is written once, correctly rounded (round to nearest, ties to even) from the exact
- * three-term sum. gradWeight is accumulated in fp32 partials and reduced in fp64 in a fixed order,
- * then rounded to the dtype, so repeated calls with the same inputs give bit-identical outputs
+ * three-term sum. gradWeight is accumulated in fp64 and reduced in a fixed order, then rounded
+ * once to the dtype, so repeated calls with the same inputs give bit-identical outputs
  * (constraints section: deterministic by default). Both outputs are overwritten, never accumulated.
  *
  * Preconditions that are NOT checked (constraints section): inputs contain no inf or NaN, and
@@ -99,8 +99,9 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
 /* The tiling chosen for a shape; a pure function of (S, B, H, dtype). Exposed so that tests can
  * place edge cases on tile boundaries. */
 typedef struct {
-    int64_t rows_per_wave;   /* rows of [S, B*H] one wavefront walks */
-    int64_t rows_per_strip;  /* rows per fused-kernel block (waves_per_block * rows_per_wave) */
+    int64_t rows_per_turn;   /* rows one wavefront handles per round */
+    int64_t rows_per_round;  /* rows a fused-kernel block advances per round */
+    int64_t rows_per_strip;  /* rows of [S, B*H] one fused-kernel block covers (whole rounds) */
     int64_t n_strips;        /* ceil(S / rows_per_strip) */
     int64_t cols_per_block;  /* columns of [S, B*H] one fused-kernel block covers */
     int64_t n_col_blocks;    /* ceil(B*H / cols_per_block) */

@@ -16,7 +16,8 @@ class MccbError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("rows_per_wave", ctypes.c_int64), ("rows_per_strip", ctypes.c_int64),
+    _fields_ = [("rows_per_turn", ctypes.c_int64), ("rows_per_round", ctypes.c_int64),
+                ("rows_per_strip", ctypes.c_int64),
                 ("n_strips", ctypes.c_int64), ("cols_per_block", ctypes.c_int64),
                 ("n_col_blocks", ctypes.c_int64), ("waves_per_block", ctypes.c_int64),
                 ("workspace_size", ctypes.c_uint64)]

@@ -11,15 +11,22 @@
 // c = j*H + h never mixes with another column except that gradWeight sums the columns that share h.
 // So the whole op is a 3-tap stencil down the rows of that matrix plus a column-group reduction.
 //
-// Kernel 1 (fused): a lane owns kVec consecutive columns (one vector load) and walks a run of rows,
-// keeping the two previous masked gradY rows in registers; per row it reads one gradY row (two
-// ahead) and one x row and writes one gradX row, so HBM sees a single streaming pass. A block
-// stacks kWaves wavefronts on the same 64*kVec columns over consecutive row runs (a "strip"). The
-// strip's mask bytes are staged in LDS once. Each lane accumulates its gradWeight terms in fp64;
-// the block sums its waves in LDS in a fixed order and writes one fp64 partial per (strip, tap,
-// column) to the caller's workspace. Kernel 2 (reduce) adds the partials of each (tap, channel)
-// over strips and batches in a fixed order and rounds once. No atomics anywhere: the result bits
-// depend only on the inputs and the plan, and the plan only on (S, B, H, dtype).
+// Kernel 1 (fused): a lane owns kVec consecutive columns (one 4-byte load per row). A block is
+// kColGroups x kRing wavefronts: kColGroups waves side by side cover kColGroups*64*kVec contiguous
+// columns, and kRing waves stacked on each column group take the rows of the block's strip round
+// robin, kTurnRows rows each per round, with a block barrier per round. So at any moment a block
+// reads one contiguous stretch of each of kRing*kTurnRows consecutive rows, and all its waves
+// advance together; each row of gradY, x and gradX crosses HBM once. A wave forms gradX for its
+// kTurnRows rows from the masked gradY rows i..i+kTurnRows+1 it holds in registers (the first two
+// are the previous wave's last look-ahead rows, loaded again and served from L2), and accumulates
+// its gradWeight terms in fp64 across all its rounds. Rounds are software-pipelined: a wave issues
+// the loads of its next turn before computing the current one, so HBM requests stay in flight
+// through the arithmetic and across the (fence-free) round barrier. The strip's mask bytes are staged in LDS
+// once. At the end the block sums the kRing waves of each column group in LDS in a fixed order and
+// writes one fp64 partial per (strip, tap, column) to the caller's workspace. Kernel 2 (reduce)
+// adds the partials of each (tap, channel) over strips and batches in a fixed order and rounds
+// once. No atomics anywhere: the result bits depend only on the inputs and the plan, and the plan
+// only on (S, B, H, dtype).
 //
 // Precision: every product of two 16-bit values is exact in fp64 (and in fp32). gradX's three
 // products are summed in fp64 in the equation's order and the sum is rounded once to the dtype
@@ -37,22 +44,34 @@
 
 // Tuning constants (compile-time; every value here gives the same results).
 #ifndef MCCB_VEC
-#define MCCB_VEC 4  // columns per lane: 4 -> 8-byte loads, 8 -> 16-byte loads
+#define MCCB_VEC 2  // columns per lane: 2 -> 4-byte loads, 4 -> 8-byte loads
 #endif
-#ifndef MCCB_UNROLL
-#define MCCB_UNROLL 4  // rows whose loads a lane keeps in flight
+#ifndef MCCB_COL_GROUPS
+#define MCCB_COL_GROUPS 4  // waves side by side in a block (each 64 lanes x MCCB_VEC columns)
 #endif
-#ifndef MCCB_WAVES
-#define MCCB_WAVES 4  // wavefronts per fused block, stacked along rows
+#ifndef MCCB_RING
+#define MCCB_RING 2  // waves stacked along rows in a block, taking rows round robin
+#endif
+#ifndef MCCB_TURN_ROWS
+#define MCCB_TURN_ROWS 8  // rows a wave handles per round (loads kept in flight together)
 #endif
 #ifndef MCCB_NT_LOAD
-#define MCCB_NT_LOAD 1  // streaming (non-temporal) hint on gradY / x loads
+#define MCCB_NT_LOAD 1  // streaming (non-temporal) hint on gradY / x loads read once
 #endif
 #ifndef MCCB_NT_STORE
 #define MCCB_NT_STORE 1  // streaming (non-temporal) hint on gradX stores
 #endif
-#ifndef MCCB_TARGET_WAVES
-#define MCCB_TARGET_WAVES 16384  // grid size (in waves) above which row runs get longer
+#ifndef MCCB_WAVES_PER_SIMD
+#define MCCB_WAVES_PER_SIMD 4  // occupancy the fused kernel is compiled for (caps its VGPRs)
+#endif
+#ifndef MCCB_EXACT_GRADX
+#define MCCB_EXACT_GRADX 1  // 1: gradX correctly rounded from fp64; 0: fp64 -> fp32 -> dtype
+#endif
+#ifndef MCCB_ROUND_BARRIER
+#define MCCB_ROUND_BARRIER 1  // keep a block's waves on the same round
+#endif
+#ifndef MCCB_TARGET_BLOCKS
+#define MCCB_TARGET_BLOCKS 2048  // the plan splits rows into strips until the grid has this many blocks
 #endif
 
 namespace {
@@ -63,23 +82,28 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;  // lanes per wavefront on CDNA
-constexpr int kVec = MCCB_VEC;
-constexpr int kWords = kVec / 2;  // 32-bit words per lane vector (two 16-bit values each)
-constexpr int kUnroll = MCCB_UNROLL;
-constexpr int kWaves = MCCB_WAVES;
-constexpr int kBlockCols = kWave * kVec;
+constexpr int kVec = MCCB_VEC;  // columns per lane: one load of kVec 16-bit values
+constexpr int kWords = kVec / 2;
+constexpr int kColGroups = MCCB_COL_GROUPS;
+constexpr int kRing = MCCB_RING;
+constexpr int kTurnRows = MCCB_TURN_ROWS;
+constexpr int kBlockWaves = kColGroups * kRing;
+constexpr int kGroupCols = kWave * kVec;             // columns of one column group
+constexpr int kBlockCols = kColGroups * kGroupCols;  // columns of one block
+constexpr int kRoundRows = kRing * kTurnRows;        // rows a block advances per round
 constexpr int kMaxBatchesPerBlock = 3;  // 512 or fewer columns span at most 3 batches if H >= 384
 constexpr int kReduceWaves = 16;        // wavefronts per reduce block
 constexpr int kReduceCols = kWave * 2;  // channels per reduce block (2 fp64 per lane)
-static_assert(kVec == 4 || kVec == 8, "lane vector must be 8 or 16 bytes");
+static_assert(kVec == 2 || kVec == 4, "lane vector must be 4 or 8 bytes");
 static_assert(kBlockCols <= 512, "mask staging assumes a block spans at most 3 batches");
+static_assert(kBlockWaves * kWave <= 1024, "block too large");
 
 typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
 
 constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
-constexpr int64_t kMinRowsPerWave = 64, kMaxRowsPerWave = 1024;
-constexpr int64_t kTargetWaves = MCCB_TARGET_WAVES;
+constexpr int64_t kTargetBlocks = MCCB_TARGET_BLOCKS;
+constexpr int64_t kMaxMaskLds = 48 * 1024;  // bytes of LDS for the staged mask, at most
 
 // ---------------------------------------------------------------------------------------------
 // 16-bit formats
@@ -136,6 +160,7 @@ __device__ static inline vec_t load_vec(const vec_t *p) {
     return *p;
 #endif
 }
+__device__ static inline vec_t load_vec_cached(const vec_t *p) { return *p; }
 __device__ static inline void store_vec(vec_t *p, vec_t v) {
 #if MCCB_NT_STORE
     __builtin_nontemporal_store(v, p);
@@ -161,7 +186,11 @@ __device__ static inline vec_t stencil_row(const double (&d0)[kVec], const doubl
         double s = d0[e] * w2[e];
         s = __builtin_fma(d1[e], w1[e], s);
         s = __builtin_fma(d2[e], w0[e], s);
+#if MCCB_EXACT_GRADX
         out[e] = round_to_odd_f32(s);
+#else
+        out[e] = (float)s;
+#endif
         // gradWeight[k] += gYm[i+2-k] * x[i]
         const double xd = (double)xf[e];
         a2[e] = __builtin_fma(d0[e], xd, a2[e]);
@@ -184,32 +213,35 @@ __device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
 
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: mask + gradX + gradWeight partials in one HBM pass.
-// grid.x = n_col_blocks * n_strips (column block fastest), block = kWaves * 64 lanes.
+// grid.x = n_col_blocks * n_strips (column block fastest), block = kColGroups * kRing waves.
 // Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + 2) mask bytes.
 // Workspace: fp64 partials [n_strips][3][C].
 // ---------------------------------------------------------------------------------------------
 template <int DT, bool HAS_MASK>
-__global__ void __launch_bounds__(kWaves *kWave)
+__global__ void __launch_bounds__(kBlockWaves *kWave)
+    __attribute__((amdgpu_waves_per_eu(MCCB_WAVES_PER_SIMD)))
     mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
                    const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
                    vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
-                   int64_t rows_per_wave, int64_t n_col_blocks) {
+                   int64_t rows_per_strip, int64_t n_col_blocks) {
     extern __shared__ uint8_t smask[];
-    __shared__ f64x2 red[kWaves][kBlockCols / 2];
+    __shared__ f64x2 red[kBlockWaves][kWave * kVec / 2];
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane of a wave; saying so keeps everything derived from
     // it (row ranges, row addresses) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int ring = wave / kColGroups;  // position along rows
+    const int group = wave % kColGroups;  // column group
     const int64_t C = B * H;
     const int64_t CV = C / kVec;  // lane vectors per row
     const int64_t col_block = blockIdx.x % n_col_blocks;
     const int64_t strip = blockIdx.x / n_col_blocks;
-    const int64_t T = rows_per_wave * kWaves;
-    const int64_t strip_row0 = strip * T;
+    const int64_t rs0 = strip * rows_per_strip;
+    const int64_t rs1 = (rs0 + rows_per_strip < S) ? rs0 + rows_per_strip : S;
 
     // Lanes past the last column load a valid column (the last one) and store nothing.
-    const int64_t v_raw = col_block * kWave + lane;
+    const int64_t v_raw = (col_block * kColGroups + group) * kWave + lane;
     const bool active = v_raw < CV;
     const int64_t v = active ? v_raw : CV - 1;
     const int64_t c = v * kVec;
@@ -222,10 +254,10 @@ __global__ void __launch_bounds__(kWaves *kWave)
         const int64_t c_last = (c_first + kBlockCols < C ? c_first + kBlockCols : C) - 1;
         const int64_t j_first = c_first / H;
         const int nj = (int)(c_last / H - j_first + 1);
-        const int span = (int)(T + 2);
+        const int span = (int)(rows_per_strip + 2);
         for (int t = threadIdx.x; t < nj * span; t += blockDim.x) {
             const int jj = t / span;
-            const int64_t row = strip_row0 + (t - jj * span);
+            const int64_t row = rs0 + (t - jj * span);
             smask[t] = (row < S) ? mask[(j_first + jj) * S + row] : (uint8_t)0;
         }
         moff = (int)(j - j_first) * span;
@@ -250,95 +282,125 @@ __global__ void __launch_bounds__(kWaves *kWave)
 #pragma unroll
     for (int e = 0; e < kVec; ++e) a0[e] = a1[e] = a2[e] = 0.0;
 
-    const int64_t r_begin = strip_row0 + wave * rows_per_wave;
-    const int64_t r_end = (r_begin + rows_per_wave < S) ? r_begin + rows_per_wave : S;
     vec_t zero;
 #pragma unroll
     for (int p = 0; p < kWords; ++p) zero[p] = 0u;
-
-    // Masked gradY row `row` (zero past the end).
-    auto masked_row = [&](int64_t row) -> vec_t {
-        if (row >= S) return zero;
-        vec_t q = load_vec(gy + row * CV + v);
-        if constexpr (HAS_MASK) {
-            if (smask[moff + (int)(row - strip_row0)] == 0) q = zero;
-        }
-        return q;
+    // Whether the mask keeps gradY row `row` of this lane's batch (rows < S only).
+    auto keep = [&](int64_t row) -> bool {
+        if constexpr (HAS_MASK) return smask[moff + (int)(row - rs0)] != 0;
+        return true;
     };
 
-    if (r_begin < r_end) {
-        // dw[0], dw[1]: masked gradY rows i, i+1 in fp64, carried across iterations.
-        double dw[kUnroll + 2][kVec];
-        widen<DT>(masked_row(r_begin), dw[0]);
-        widen<DT>(masked_row(r_begin + 1), dw[1]);
+    // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
+    // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
+    const int64_t row_bytes = C * 2;
+    const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
+    auto at = [&](const vec_t *base, int64_t row) -> const vec_t * {
+        return reinterpret_cast<const vec_t *>(reinterpret_cast<const char *>(base) +
+                                               row * row_bytes + lane_off);
+    };
+    auto out_at = [&](int64_t row) -> vec_t * {
+        return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx) + row * row_bytes + lane_off);
+    };
 
-        // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
-        // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
-        const int64_t row_bytes = C * 2;
-        const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
-        const char *gy_rows = reinterpret_cast<const char *>(gy) + (r_begin + 2) * row_bytes;
-        const char *x_rows = reinterpret_cast<const char *>(x) + r_begin * row_bytes;
-        char *gx_rows = reinterpret_cast<char *>(gx) + r_begin * row_bytes;
-
-        int64_t i = r_begin;
-        // Steady state: rows i .. i+kUnroll-1 and their look-ahead rows all lie inside [0, S).
-        for (; i + kUnroll <= r_end && i + kUnroll + 2 <= S; i += kUnroll) {
-            vec_t qy[kUnroll], qx[kUnroll];
+    // A turn is "whole" when this wave's kTurnRows rows and their look-ahead rows all exist.
+    auto whole = [&](int64_t r0) {
+        const int64_t i0 = r0 + ring * kTurnRows;
+        return i0 + kTurnRows <= rs1 && i0 + kTurnRows + 2 <= S;
+    };
+    // Issue the loads of a whole turn: gradY rows i0 .. i0+kTurnRows+1 and x rows i0 ..
+    // i0+kTurnRows-1. Rows i0, i0+1 were the previous wave's last look-ahead rows, and this wave's
+    // last two are the next wave's first: cached loads, so those come from L2; the rest stream.
+    auto issue = [&](int64_t r0, vec_t (&qy)[kTurnRows + 2], vec_t (&qx)[kTurnRows]) {
+        const int64_t i0 = r0 + ring * kTurnRows;
+        qy[0] = load_vec_cached(at(gy, i0));
+        qy[1] = load_vec_cached(at(gy, i0 + 1));
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                qy[u] = load_vec(reinterpret_cast<const vec_t *>(gy_rows + u * row_bytes + lane_off));
-                qx[u] = load_vec(reinterpret_cast<const vec_t *>(x_rows + u * row_bytes + lane_off));
-            }
+        for (int u = 0; u < kTurnRows; ++u) {
+            qy[u + 2] = (u + 2 >= kTurnRows) ? load_vec_cached(at(gy, i0 + 2 + u))
+                                             : load_vec(at(gy, i0 + 2 + u));
+            qx[u] = load_vec(at(x, i0 + u));
+        }
+    };
+    auto compute = [&](int64_t r0, const vec_t (&qy)[kTurnRows + 2], const vec_t (&qx)[kTurnRows]) {
+        const int64_t i0 = r0 + ring * kTurnRows;
+        double d0[kVec], d1[kVec], d2[kVec];
+        widen<DT>(keep(i0) ? qy[0] : zero, d0);
+        widen<DT>(keep(i0 + 1) ? qy[1] : zero, d1);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                vec_t q = qy[u];
-                if constexpr (HAS_MASK) {
-                    if (smask[moff + (int)(i + 2 + u - strip_row0)] == 0) q = zero;
-                }
-                widen<DT>(q, dw[u + 2]);
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const vec_t r =
-                    stencil_row<DT>(dw[u], dw[u + 1], dw[u + 2], qx[u], w0, w1, w2, a0, a1, a2);
-                if (active) store_vec(reinterpret_cast<vec_t *>(gx_rows + u * row_bytes + lane_off), r);
-            }
+        for (int u = 0; u < kTurnRows; ++u) {
+            widen<DT>(keep(i0 + 2 + u) ? qy[u + 2] : zero, d2);
+            const vec_t r = stencil_row<DT>(d0, d1, d2, qx[u], w0, w1, w2, a0, a1, a2);
+            if (active) store_vec(out_at(i0 + u), r);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
-                dw[0][e] = dw[kUnroll][e];
-                dw[1][e] = dw[kUnroll + 1][e];
+                d0[e] = d1[e];
+                d1[e] = d2[e];
             }
-            gy_rows += kUnroll * row_bytes;
-            x_rows += kUnroll * row_bytes;
-            gx_rows += kUnroll * row_bytes;
         }
-        // Tail: one row at a time; look-ahead rows past S read as zero.
-        for (; i < r_end; ++i) {
-            widen<DT>(masked_row(i + 2), dw[2]);
-            const vec_t r = stencil_row<DT>(dw[0], dw[1], dw[2], load_vec(x + i * CV + v), w0, w1,
-                                            w2, a0, a1, a2);
-            if (active) store_vec(gx + i * CV + v, r);
+    };
+    // Partial turn at the end of the strip or of the tensor: one row at a time, gradY rows past S
+    // read as zero.
+    auto partial = [&](int64_t r0) {
+        const int64_t i0 = r0 + ring * kTurnRows;
+        if (i0 >= rs1) return;
+        const int64_t i1 = (i0 + kTurnRows < rs1) ? i0 + kTurnRows : rs1;
+        double d0[kVec], d1[kVec], d2[kVec];
+        widen<DT>((i0 < S && keep(i0)) ? load_vec_cached(at(gy, i0)) : zero, d0);
+        widen<DT>((i0 + 1 < S && keep(i0 + 1)) ? load_vec_cached(at(gy, i0 + 1)) : zero, d1);
+        for (int64_t i = i0; i < i1; ++i) {
+            widen<DT>((i + 2 < S && keep(i + 2)) ? load_vec_cached(at(gy, i + 2)) : zero, d2);
+            const vec_t r = stencil_row<DT>(d0, d1, d2, load_vec(at(x, i)), w0, w1, w2, a0, a1, a2);
+            if (active) store_vec(out_at(i), r);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
-                dw[0][e] = dw[1][e];
-                dw[1][e] = dw[2][e];
+                d0[e] = d1[e];
+                d1[e] = d2[e];
             }
         }
+    };
+    // One round: prefetch the next round's whole turn into `nxt`, then compute this round from
+    // `cur` (loaded one round earlier) while those loads are in flight.
+    auto round = [&](int64_t r0, const vec_t (&cy)[kTurnRows + 2], const vec_t (&cx)[kTurnRows],
+                     vec_t (&ny)[kTurnRows + 2], vec_t (&nx)[kTurnRows]) {
+        const int64_t rn = r0 + kRoundRows;
+        if (rn < rs1 && whole(rn)) issue(rn, ny, nx);
+        if (whole(r0))
+            compute(r0, cy, cx);
+        else
+            partial(r0);
+#if MCCB_ROUND_BARRIER
+        // Keep the block's waves on the same round. A bare barrier, without a memory fence, so
+        // the prefetched loads stay in flight across it.
+        __builtin_amdgcn_s_barrier();
+#endif
+    };
+
+    vec_t ay[kTurnRows + 2], ax[kTurnRows], by[kTurnRows + 2], bx[kTurnRows];
+    if (whole(rs0)) issue(rs0, ay, ax);
+    // Unrolled by two so that the two register buffers swap roles without copies.
+    for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * kRoundRows) {
+        round(r0, ay, ax, by, bx);
+        if (r0 + kRoundRows >= rs1) break;
+        round(r0 + kRoundRows, by, bx, ay, ax);
     }
 
-    // gradWeight partials of the strip: add the kWaves waves in a fixed order (wave 0 first).
+    // gradWeight partials of the strip: for each column group add its kRing waves in a fixed
+    // order (ring position 0 first).
     const int64_t col0 = col_block * kBlockCols;
     for (int k = 0; k < 3; ++k) {
         const double *acc = (k == 0) ? a0 : (k == 1) ? a1 : a2;
         __syncthreads();
 #pragma unroll
-        for (int p = 0; p < kVec / 2; ++p) red[wave][lane * (kVec / 2) + p] = f64x2{acc[2 * p], acc[2 * p + 1]};
+        for (int p = 0; p < kVec / 2; ++p)
+            red[wave][lane * (kVec / 2) + p] = f64x2{acc[2 * p], acc[2 * p + 1]};
         __syncthreads();
         const double *flat = reinterpret_cast<const double *>(&red[0][0]);
         for (int t = threadIdx.x; t < kBlockCols; t += blockDim.x) {
-            double s = flat[t];
+            const int g = t / kGroupCols, within = t - g * kGroupCols;
+            double s = flat[g * kGroupCols + within];
 #pragma unroll
-            for (int q = 1; q < kWaves; ++q) s += flat[q * kBlockCols + t];
+            for (int q = 1; q < kRing; ++q) s += flat[(q * kColGroups + g) * kGroupCols + within];
             const int64_t col = col0 + t;
             if (col < C) ws[(strip * 3 + k) * C + col] = s;
         }
@@ -394,8 +456,9 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
 struct Plan {
     int64_t S, B, H, C;
     int dtype;
-    int64_t rows_per_wave, rows_per_strip, n_strips, n_col_blocks;
+    int64_t rows_per_strip, n_strips, n_col_blocks;
     uint64_t ws_bytes;
+    size_t mask_lds;
 };
 
 int check_shape(int64_t S, int64_t B, int64_t H, int dtype) {
@@ -415,18 +478,21 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype) {
     p.C = B * H;
     p.dtype = dtype;
     p.n_col_blocks = (p.C + kBlockCols - 1) / kBlockCols;
-    // Start at kMinRowsPerWave rows per wave and double while the grid keeps at least
-    // kTargetWaves waves: longer row runs cut the partial traffic (16 bytes per column per strip
-    // written and read back, against 6 bytes per element streamed) and the 2-row look-ahead
-    // re-read at the end of every run.
-    auto waves_for = [&](int64_t rpw) {
-        const int64_t strips = (S + rpw * kWaves - 1) / (rpw * kWaves);
-        return strips * p.n_col_blocks * kWaves;
-    };
-    int64_t r = kMinRowsPerWave;
-    while (r < kMaxRowsPerWave && waves_for(2 * r) >= kTargetWaves) r *= 2;
-    p.rows_per_wave = r;
-    p.rows_per_strip = r * kWaves;
+    // Split the rows into strips until the grid has about kTargetBlocks blocks (enough to fill
+    // the GPU several times over), with strips a whole number of rounds long. Fewer, longer strips
+    // cut the partial traffic: 24 bytes per column per strip written and read back, against 6
+    // bytes per element streamed.
+    const int64_t max_strips = (S + kRoundRows - 1) / kRoundRows;
+    int64_t strips = (kTargetBlocks + p.n_col_blocks - 1) / p.n_col_blocks;
+    if (strips > max_strips) strips = max_strips;
+    if (strips < 1) strips = 1;
+    for (;;) {
+        const int64_t rows = (S + strips - 1) / strips;
+        p.rows_per_strip = (rows + kRoundRows - 1) / kRoundRows * kRoundRows;
+        p.mask_lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + 2);
+        if (p.mask_lds <= (size_t)kMaxMaskLds || strips >= max_strips) break;
+        ++strips;  // keep the staged mask within its LDS budget
+    }
     p.n_strips = (S + p.rows_per_strip - 1) / p.rows_per_strip;
     p.ws_bytes = (uint64_t)p.n_strips * 3u * (uint64_t)p.C * sizeof(double);
     return p;
@@ -451,17 +517,17 @@ template <int DT>
 hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, const uint8_t *mask,
                   void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev) {
     const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
-    const dim3 block1(kWaves * kWave);
+    const dim3 block1(kBlockWaves * kWave);
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
     if (mask) {
-        const size_t lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + 2);
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1, lds, st, (const vec_t *)gy,
-                           (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx, (double *)ws,
-                           p.S, p.B, p.H, p.rows_per_wave, p.n_col_blocks);
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1, p.mask_lds, st,
+                           (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask,
+                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
+                           p.n_col_blocks);
     } else {
         hipLaunchKernelGGL((mccb_fused_bwd<DT, false>), grid1, block1, 0, st, (const vec_t *)gy,
                            (const vec_t *)x, (const vec_t *)w, (const uint8_t *)nullptr,
-                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_wave,
+                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
                            p.n_col_blocks);
     }
     hipError_t e = hipGetLastError();
@@ -493,12 +559,13 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     const int rc = check_shape(S, B, H, dtype);
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype);
-    plan->rows_per_wave = p.rows_per_wave;
+    plan->rows_per_turn = kTurnRows;
+    plan->rows_per_round = kRoundRows;
     plan->rows_per_strip = p.rows_per_strip;
     plan->n_strips = p.n_strips;
     plan->cols_per_block = kBlockCols;
     plan->n_col_blocks = p.n_col_blocks;
-    plan->waves_per_block = kWaves;
+    plan->waves_per_block = kBlockWaves;
     plan->workspace_size = p.ws_bytes;
     return MCCB_OK;
 }

@@ -143,7 +143,7 @@ def compare_rows(wl, gx, rows: np.ndarray, tag=None):
 def sample_rows(wl, plan: dict, n_random: int = 6, seed: int = 1) -> np.ndarray:
     S = wl.S
     rng = np.random.default_rng(seed)
-    R, T = plan["rows_per_wave"], plan["rows_per_strip"]
+    R, T = plan["rows_per_turn"], plan["rows_per_strip"]
     cand = {0, 1, 2, S - 3, S - 2, S - 1, R - 1, R, R + 1, T - 2, T - 1, T, T + 1, 2 * T - 1}
     cand.update(int(r) for r in rng.integers(0, S, n_random))
     return np.array(sorted(r for r in cand if 0 <= r < S), dtype=np.int64)

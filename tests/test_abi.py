@@ -130,7 +130,8 @@ def test_plan_is_pure_and_consistent():
         p2 = mdc.mccb_get_plan(S, B, H, dt)
         assert p1 == p2
         C = B * H
-        assert p1["rows_per_strip"] == p1["rows_per_wave"] * p1["waves_per_block"]
+        assert p1["rows_per_strip"] % p1["rows_per_round"] == 0
+        assert p1["rows_per_round"] % p1["rows_per_turn"] == 0
         assert p1["n_strips"] == -(-S // p1["rows_per_strip"])
         assert p1["n_col_blocks"] == -(-C // p1["cols_per_block"])
         assert p1["workspace_size"] == p1["n_strips"] * 3 * C * 8

@@ -84,11 +84,19 @@ def test_tile_boundaries_full():
     """S on and around the strip and wave-run boundaries the plan picks for this shape."""
     B, H = 2, 384
     base = mdc.mccb_get_plan(4096, B, H, mdc.MCCB_BF16)
-    R, T = base["rows_per_wave"], base["rows_per_strip"]
-    for S in sorted({R - 1, R + 1, R + 2, T - 1, T, T + 1, T + 2, 2 * T + 3}):
+    R, Q = base["rows_per_turn"], base["rows_per_round"]
+    cases = {R - 1, R + 1, R + 2, Q - 1, Q, Q + 1, Q + 2, 2 * Q + 3}
+    for S in sorted(cases):
+        # the strip length follows S; also check S just around the strip of a longer tensor
         wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S)
         gx, gw = gpu_run(wl)
-        compare_full(wl, gx, gw, tag=f"S={S} (R={R}, T={T})")
+        compare_full(wl, gx, gw, tag=f"S={S} (turn {R}, round {Q})")
+    T = base["rows_per_strip"]
+    for S in (4096, T + 1, T + R + 3):
+        wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S + 1)
+        p = mdc.mccb_get_plan(S, B, H, mdc.MCCB_BF16)
+        gx, gw = gpu_run(wl)
+        compare_full(wl, gx, gw, tag=f"S={S} (strip {p['rows_per_strip']} x {p['n_strips']})")
 
 
 def test_subnormal_outputs_full():
