@@ -70,8 +70,17 @@
 #ifndef MCCB_ROUND_BARRIER
 #define MCCB_ROUND_BARRIER 1  // keep a block's waves on the same round
 #endif
-#ifndef MCCB_TARGET_BLOCKS
-#define MCCB_TARGET_BLOCKS 2048  // the plan splits rows into strips until the grid has this many blocks
+#ifndef MCCB_LDS_FLOOR
+#define MCCB_LDS_FLOOR 0  // dynamic LDS bytes the fused kernel reserves at least (caps blocks per CU)
+#endif
+#ifndef MCCB_STRIP_ROWS
+#define MCCB_STRIP_ROWS 768  // the plan aims for strips about this many rows long ...
+#endif
+#ifndef MCCB_MIN_BLOCKS
+#define MCCB_MIN_BLOCKS 2048  // ... splitting further until the grid has this many blocks ...
+#endif
+#ifndef MCCB_MIN_STRIP_ROWS
+#define MCCB_MIN_STRIP_ROWS 128  // ... but not below this many rows per strip
 #endif
 
 namespace {
@@ -102,7 +111,9 @@ typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
 
 constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
-constexpr int64_t kTargetBlocks = MCCB_TARGET_BLOCKS;
+constexpr int64_t kStripRows = MCCB_STRIP_ROWS;
+constexpr int64_t kMinBlocks = MCCB_MIN_BLOCKS;
+constexpr int64_t kMinStripRows = MCCB_MIN_STRIP_ROWS;
 constexpr int64_t kMaxMaskLds = 48 * 1024;  // bytes of LDS for the staged mask, at most
 
 // ---------------------------------------------------------------------------------------------
@@ -478,12 +489,18 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype) {
     p.C = B * H;
     p.dtype = dtype;
     p.n_col_blocks = (p.C + kBlockCols - 1) / kBlockCols;
-    // Split the rows into strips until the grid has about kTargetBlocks blocks (enough to fill
-    // the GPU several times over), with strips a whole number of rounds long. Fewer, longer strips
-    // cut the partial traffic: 24 bytes per column per strip written and read back, against 6
-    // bytes per element streamed.
+    // Split the rows into strips of about kStripRows rows, more if the grid would have fewer than
+    // kMinBlocks blocks (too few to keep every CU busy), but none shorter than kMinStripRows rows;
+    // strips are a whole number of rounds long. Short-lived blocks keep the rows in flight across
+    // the GPU close together, which the HBM serves faster than long independent column walks; each
+    // strip costs 24 bytes per column of partials written and read back, against 6 bytes per
+    // element streamed.
     const int64_t max_strips = (S + kRoundRows - 1) / kRoundRows;
-    int64_t strips = (kTargetBlocks + p.n_col_blocks - 1) / p.n_col_blocks;
+    int64_t strips = (S + kStripRows - 1) / kStripRows;
+    const int64_t fill = (kMinBlocks + p.n_col_blocks - 1) / p.n_col_blocks;
+    if (strips < fill) strips = fill;
+    const int64_t shortest = (S + kMinStripRows - 1) / kMinStripRows;
+    if (strips > shortest) strips = shortest;
     if (strips > max_strips) strips = max_strips;
     if (strips < 1) strips = 1;
     for (;;) {
@@ -518,14 +535,16 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
                   void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev) {
     const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
     const dim3 block1(kBlockWaves * kWave);
+    const size_t lds_floor = MCCB_LDS_FLOOR;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
     if (mask) {
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1, p.mask_lds, st,
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1,
+                           p.mask_lds > lds_floor ? p.mask_lds : lds_floor, st,
                            (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask,
                            (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
                            p.n_col_blocks);
     } else {
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, false>), grid1, block1, 0, st, (const vec_t *)gy,
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, false>), grid1, block1, lds_floor, st, (const vec_t *)gy,
                            (const vec_t *)x, (const vec_t *)w, (const uint8_t *)nullptr,
                            (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
                            p.n_col_blocks);

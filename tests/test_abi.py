@@ -142,8 +142,9 @@ def test_plan_is_pure_and_consistent():
 
 
 def test_workspace_stays_small_at_the_headline_shape():
-    # fp64 partials: bounded well below 1 % of the 16.1 GB streamed at S=16384, B=32, H=5120
-    assert _ws(16384, 32, 5120) < 0.005 * 3 * 16384 * 32 * 5120 * 2
+    # fp64 partials, written once and read once: below 1 % of the 16.1 GB streamed at
+    # S=16384, B=32, H=5120, so at most 2 % extra traffic
+    assert _ws(16384, 32, 5120) < 0.01 * 3 * 16384 * 32 * 5120 * 2
 
 
 def test_status_strings():
