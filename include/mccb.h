@@ -96,8 +96,32 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
                   void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
                   void *workspace, uint64_t workspace_size, void *stream);
 
-/* The tiling chosen for a shape; a pure function of (S, B, H, dtype). Exposed so that tests can
- * place edge cases on tile boundaries. */
+/*
+ * The forward operation whose gradients mccb_backward computes: the masked causal depthwise
+ * convolution named beside the backward on the same page (the MaskedCausalConv1d operator),
+ *
+ *   y[i,j] = mask[j,i] * sum_{k=0}^{2} weight[k] * x[i-2+k, j]      (x rows < 0 are zero),
+ *
+ * per channel h, i.e. the operator whose adjoint in x is the gradX equation above and whose
+ * derivative in weight is the gradWeight equation. The page documents only the backward; this
+ * reading of the forward is the one its three equations imply.
+ *
+ *   x      : input [S,B,H], device memory, 16-byte aligned, not modified
+ *   weight : input [3,H], device memory, 16-byte aligned
+ *   mask   : optional [B,S] bytes as for mccb_backward (NULL = all true); masked outputs are 0
+ *   y      : output [S,B,H], device memory, 16-byte aligned, overwritten; must not overlap x,
+ *            weight or mask
+ *
+ * Each output is the exact three-term sum rounded once to nearest-even in the dtype. Same shape
+ * limits and error codes as mccb_backward; needs no workspace. Enqueues on `stream` (NULL = the
+ * default stream) and returns without waiting; MCCB_ERR_RUNTIME reports a failed launch.
+ */
+int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
+                 int64_t B, int64_t H, int dtype, void *stream);
+
+/* The tiling chosen for a shape, for mccb_backward (first eight fields) and mccb_forward (fwd_*);
+ * a pure function of (S, B, H, dtype). Exposed so that tests can place edge cases on tile
+ * boundaries. */
 typedef struct {
     int64_t rows_per_turn;   /* rows one wavefront handles per round */
     int64_t rows_per_round;  /* rows a fused-kernel block advances per round */
@@ -107,6 +131,10 @@ typedef struct {
     int64_t n_col_blocks;    /* ceil(B*H / cols_per_block) */
     int64_t waves_per_block;
     uint64_t workspace_size; /* same value as mccb_get_workspace_size */
+    int64_t fwd_rows_per_tile; /* rows one mccb_forward block covers */
+    int64_t fwd_cols_per_tile; /* columns of [S, B*H] one mccb_forward block covers */
+    int64_t fwd_n_col_tiles;   /* ceil(B*H / fwd_cols_per_tile) */
+    int64_t fwd_n_row_tiles;   /* ceil(S / fwd_rows_per_tile) */
 } mccb_plan_t;
 
 /* Fills *plan for a valid shape. Same return codes as mccb_get_workspace_size. Host-only. */

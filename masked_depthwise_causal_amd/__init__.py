@@ -6,7 +6,8 @@ device memory and streams.
 
 The operation is the one on the page "aclnnMaskedCausalConv1dBackward", section 功能说明
 (function description): gradX and gradWeight of a depthwise causal conv1d over [S,B,H] tensors with a
-[3,H] weight and an optional [B,S] bool mask.
+[3,H] weight and an optional [B,S] bool mask. ``forward`` runs that conv itself (the
+MaskedCausalConv1d operator the page names beside the backward).
 """
 from __future__ import annotations
 
@@ -49,6 +50,12 @@ def mccb_backward(gradY: int, x: int, weight: int, mask: int | None, gradX: int,
     """Raw call with integer device addresses; returns the status code (does not raise)."""
     return int(lib().mccb_backward(gradY, x, weight, mask, gradX, gradWeight, S, B, H, dtype,
                                    workspace, workspace_size, stream))
+
+
+def mccb_forward(x: int, weight: int, mask: int | None, y: int, S: int, B: int, H: int, dtype: int,
+                 stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_forward(x, weight, mask, y, S, B, H, dtype, stream))
 
 
 def mccb_status_string(status: int) -> str:
@@ -127,3 +134,31 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     if rc != MCCB_OK:
         raise MccbError(rc, "mccb_backward")
     return gradX, gradWeight
+
+
+def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = None,
+            y: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """y [S,B,H] = mask * causal depthwise conv(x, weight) for contiguous device tensors (y
+    allocated if None). Enqueues on `stream` (default: torch's current stream) without
+    synchronizing."""
+    if x.dim() != 3:
+        raise ValueError("x must be [S,B,H]")
+    S, B, H = (int(s) for s in x.shape)
+    dev, dt = x.device, x.dtype
+    if dt not in DTYPE_CODE:
+        raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
+    _check_tensor("x", x, (S, B, H), dt, dev)
+    _check_tensor("weight", weight, (3, H), dt, dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (B, S), None, dev)
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be bool or uint8")
+    if y is None:
+        y = torch.empty_like(x)
+    _check_tensor("y", y, (S, B, H), dt, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = mccb_forward(x.data_ptr(), weight.data_ptr(), None if mask is None else mask.data_ptr(),
+                      y.data_ptr(), S, B, H, DTYPE_CODE[dt], st.cuda_stream)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_forward")
+    return y

@@ -20,7 +20,9 @@ class Plan(ctypes.Structure):
                 ("rows_per_strip", ctypes.c_int64),
                 ("n_strips", ctypes.c_int64), ("cols_per_block", ctypes.c_int64),
                 ("n_col_blocks", ctypes.c_int64), ("waves_per_block", ctypes.c_int64),
-                ("workspace_size", ctypes.c_uint64)]
+                ("workspace_size", ctypes.c_uint64),
+                ("fwd_rows_per_tile", ctypes.c_int64), ("fwd_cols_per_tile", ctypes.c_int64),
+                ("fwd_n_col_tiles", ctypes.c_int64), ("fwd_n_row_tiles", ctypes.c_int64)]
 
 
 def lib() -> ctypes.CDLL:
@@ -38,6 +40,8 @@ def lib() -> ctypes.CDLL:
         L.mccb_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
                                     vp, u64, vp]
         L.mccb_backward.restype = ctypes.c_int
+        L.mccb_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+        L.mccb_forward.restype = ctypes.c_int
         L.mccb_status_string.argtypes = [ctypes.c_int]
         L.mccb_status_string.restype = ctypes.c_char_p
         L.mccb_profile_begin.argtypes = [ctypes.c_int]

@@ -82,6 +82,18 @@
 #ifndef MCCB_MIN_STRIP_ROWS
 #define MCCB_MIN_STRIP_ROWS 128  // ... but not below this many rows per strip
 #endif
+#ifndef MCCB_FWD_VEC
+#define MCCB_FWD_VEC 4  // forward: channels per lane (4 = 8-byte loads)
+#endif
+#ifndef MCCB_FWD_WAVES
+#define MCCB_FWD_WAVES 8  // forward: wavefronts per block, side by side across the columns
+#endif
+#ifndef MCCB_FWD_ROWS
+#define MCCB_FWD_ROWS 8  // forward: rows one block covers
+#endif
+#ifndef MCCB_FWD_LDS
+#define MCCB_FWD_LDS (82 * 1024)  // forward: LDS reserved per block (more than half a CU's 160 KB)
+#endif
 
 namespace {
 
@@ -461,6 +473,122 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
     }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Forward kernel: y[i,c] = mask[j,i] * (w[0,h] x[i-2,c] + w[1,h] x[i-1,c] + w[2,h] x[i,c]), with
+// c = j*H + h and rows i-2, i-1 < 0 read as 0 (the causal depthwise conv the backward above
+// differentiates). Pure streaming: read x, write y, nothing to reduce.
+//
+// A block covers a short tile: kFwdRows rows x kFwdCols contiguous columns (kFwdWaves wavefronts
+// side by side, kFwdVec channels per lane). Tiles are numbered row-major, column tile fastest, so
+// the blocks in flight at any moment sit on a few neighbouring rows; the HBM serves such a compact
+// front markedly faster than many independent column walks. Each block reserves more than half of
+// a CU's LDS (it uses none), so one block runs per CU: fewer, shorter-lived tiles in flight keep
+// the front tighter still. The two rows before the tile are re-read with cached loads (the tile
+// above loaded them, also cached, as its last two rows); the column-tile count is padded to a
+// multiple of the 8 XCDs so that a tile and the tile above it run on the same XCD and share its
+// L2 (padding blocks exit at once).
+//
+// Every output is the exact three-term sum (products of 16-bit values are exact in fp64) rounded
+// once: round-to-odd to fp32, then round-to-nearest-even to the dtype.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFwdVec = MCCB_FWD_VEC;
+constexpr int kFwdWords = kFwdVec / 2;
+constexpr int kFwdWaves = MCCB_FWD_WAVES;
+constexpr int kFwdRows = MCCB_FWD_ROWS;
+constexpr int kFwdCols = kFwdWaves * kWave * kFwdVec;  // columns of one tile
+constexpr int kXcds = 8;                               // XCDs of an MI355X
+static_assert(kFwdVec == 2 || kFwdVec == 4 || kFwdVec == 8, "forward lane vector: 4, 8 or 16 bytes");
+static_assert(kFwdRows >= 2, "the two look-back rows come from the tile above");
+static_assert(kFwdWaves * kWave <= 1024, "forward block too large");
+
+typedef uint32_t fvec_t __attribute__((ext_vector_type(kFwdWords)));
+
+template <int DT>
+__device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
+#pragma unroll
+    for (int p = 0; p < kFwdWords; ++p) {
+        float lo, hi;
+        Fmt<DT>::unpack(q[p], lo, hi);
+        d[2 * p] = (double)lo;
+        d[2 * p + 1] = (double)hi;
+    }
+}
+
+template <int DT, bool HAS_MASK>
+__global__ void __launch_bounds__(kFwdWaves *kWave)
+    mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
+             const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
+             int64_t H, int64_t n_ct, int64_t n_ct_pad) {
+    extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
+    if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
+    const int64_t ct = blockIdx.x % n_ct_pad;  // column tile (fastest)
+    const int64_t rt = blockIdx.x / n_ct_pad;  // row tile
+    if (ct >= n_ct) return;                    // XCD padding
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t C = B * H;
+    const int64_t c0 = ct * kFwdCols + (int64_t)wave * (kWave * kFwdVec) + lane * kFwdVec;
+    if (c0 >= C) return;  // no barrier below: lanes past the last column just leave
+    const int64_t CV = C / kFwdVec;  // lane vectors per row (C is a multiple of 64)
+    const int64_t v = c0 / kFwdVec;
+    const int64_t h0 = c0 % H;  // the lane's kFwdVec channels share one batch: H % 64 == 0
+    const int64_t j = c0 / H;
+    const int64_t r0 = rt * kFwdRows;
+
+    // x rows r0-2 .. r0+kFwdRows-1; rows outside [0, S) are zero
+    fvec_t xr[kFwdRows + 2];
+#pragma unroll
+    for (int u = 0; u < kFwdRows + 2; ++u) {
+        const int64_t row = r0 - 2 + u;
+        fvec_t q = {};
+        if (row >= 0 && row < S) {
+            const fvec_t *p = x + row * CV + v;
+            q = (u < 2 || u >= kFwdRows) ? *p : __builtin_nontemporal_load(p);
+        }
+        xr[u] = q;
+    }
+    double w0[kFwdVec], w1[kFwdVec], w2[kFwdVec];
+    widen_f<DT>(w[(0 * H + h0) / kFwdVec], w0);
+    widen_f<DT>(w[(1 * H + h0) / kFwdVec], w1);
+    widen_f<DT>(w[(2 * H + h0) / kFwdVec], w2);
+    uint8_t keep[kFwdRows];
+#pragma unroll
+    for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
+    if (HAS_MASK) {
+        const uint8_t *mrow = mask + j * S + r0;
+#pragma unroll
+        for (int u = 0; u < kFwdRows; ++u) keep[u] = (r0 + u < S) ? mrow[u] : 0;
+    }
+
+    double a[kFwdVec], b[kFwdVec], c[kFwdVec];
+    widen_f<DT>(xr[0], a);
+    widen_f<DT>(xr[1], b);
+#pragma unroll
+    for (int u = 0; u < kFwdRows; ++u) {
+        const int64_t row = r0 + u;
+        widen_f<DT>(xr[u + 2], c);
+        float out[kFwdVec];
+#pragma unroll
+        for (int e = 0; e < kFwdVec; ++e) {
+            // y[i] = w[0] x[i-2] + w[1] x[i-1] + w[2] x[i], exact in fp64, rounded once
+            double s = a[e] * w0[e];
+            s = __builtin_fma(b[e], w1[e], s);
+            s = __builtin_fma(c[e], w2[e], s);
+            out[e] = keep[u] ? round_to_odd_f32(s) : 0.0f;
+        }
+        fvec_t r;
+#pragma unroll
+        for (int p = 0; p < kFwdWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
+        if (row < S) __builtin_nontemporal_store(r, y + row * CV + v);
+#pragma unroll
+        for (int e = 0; e < kFwdVec; ++e) {
+            a[e] = b[e];
+            b[e] = c[e];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Host side: validation, plan, launch.
 // ---------------------------------------------------------------------------------------------
@@ -561,6 +689,36 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     return e;
 }
 
+// Forward grid: column tiles padded to a multiple of the XCD count, times row tiles.
+struct FwdPlan {
+    int64_t n_ct, n_ct_pad, n_rt;
+};
+
+FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
+    FwdPlan f;
+    f.n_ct = (B * H + kFwdCols - 1) / kFwdCols;
+    f.n_ct_pad = (f.n_ct + kXcds - 1) / kXcds * kXcds;
+    f.n_rt = (S + kFwdRows - 1) / kFwdRows;
+    return f;
+}
+
+template <int DT>
+hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, const void *x, const void *w,
+                      const uint8_t *mask, void *y, hipStream_t st) {
+    const FwdPlan f = make_fwd_plan(S, B, H);
+    const dim3 grid((unsigned)(f.n_ct_pad * f.n_rt));
+    const dim3 block(kFwdWaves * kWave);
+    if (mask) {
+        hipLaunchKernelGGL((mccb_fwd<DT, true>), grid, block, MCCB_FWD_LDS, st, (const fvec_t *)x,
+                           (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, f.n_ct_pad);
+    } else {
+        hipLaunchKernelGGL((mccb_fwd<DT, false>), grid, block, MCCB_FWD_LDS, st,
+                           (const fvec_t *)x, (const fvec_t *)w, (const uint8_t *)nullptr,
+                           (fvec_t *)y, S, B, H, f.n_ct, f.n_ct_pad);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -586,6 +744,11 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     plan->n_col_blocks = p.n_col_blocks;
     plan->waves_per_block = kBlockWaves;
     plan->workspace_size = p.ws_bytes;
+    const FwdPlan f = make_fwd_plan(S, B, H);
+    plan->fwd_rows_per_tile = kFwdRows;
+    plan->fwd_cols_per_tile = kFwdCols;
+    plan->fwd_n_col_tiles = f.n_ct;
+    plan->fwd_n_row_tiles = f.n_rt;
     return MCCB_OK;
 }
 
@@ -625,6 +788,24 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
         (dtype == MCCB_BF16)
             ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev)
             : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
+                 int64_t B, int64_t H, int dtype, void *stream) {
+    if (!x || !weight || !y) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(y)) return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
+    const uint64_t mb = mask ? (uint64_t)(B * S) : 0u;
+    // y must not overlap any input: a tile reads rows of x that other tiles write in y.
+    if (overlaps(y, nb, x, nb) || overlaps(y, nb, weight, wb) || (mask && overlaps(y, nb, mask, mb)))
+        return MCCB_ERR_PARAM_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = (dtype == MCCB_BF16)
+                             ? launch_fwd<MCCB_BF16>(S, B, H, x, weight, mask, y, st)
+                             : launch_fwd<MCCB_FP16>(S, B, H, x, weight, mask, y, st);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 

@@ -141,6 +141,16 @@ class Oracle:
         return y
 
 
+    def forward16(self, dtype: str, x16: np.ndarray, w16: np.ndarray,
+                  mask: np.ndarray | None) -> dict:
+        """The forward on 16-bit inputs: decode exactly, compute in fp64, round once to `dtype`
+        with the oracle's own encoder. Returns {"y64": fp64 values, "y16": rounded bit patterns}."""
+        x64 = self.decode(dtype, np.ascontiguousarray(x16, dtype=np.uint16))
+        w64 = self.decode(dtype, np.ascontiguousarray(w16, dtype=np.uint16))
+        y64 = self.forward(x64, w64, mask)
+        return {"y64": y64, "y16": self.encode(dtype, y64)}
+
+
 def _ptr(a: np.ndarray, typ):
     return a.ctypes.data_as(typ)
 

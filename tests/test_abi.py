@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mccb_get_workspace_size", "mccb_backward"):
+    for n in ("mccb_get_workspace_size", "mccb_backward", "mccb_forward"):
         assert n in names
 
 
@@ -120,6 +120,43 @@ def test_misaligned_pointer(which):
     dict(ws=GY + 4096), dict(ws=GX), dict(ws=GW), dict(gx=M - 512)])
 def test_overlapping_buffers(case):
     assert call(**case) == INVALID
+
+
+Y = GX  # the forward's output slot
+
+
+def fcall(x=X, w=W, m=M, y=Y, S=64, B=2, H=384, dt=BF16, stream=None):
+    rc = mdc.mccb_forward(x, w, m, y, S, B, H, dt, stream)
+    assert rc in VALIDATION_CODES, f"forward call passed validation with fake pointers (rc={rc})"
+    return rc
+
+
+@pytest.mark.parametrize("which", ["x", "w", "y"])
+def test_forward_null_required_pointer(which):
+    assert fcall(**{which: None}) == NULLPTR
+
+
+@pytest.mark.parametrize("dt", [-1, 2])
+def test_forward_bad_dtype(dt):
+    assert fcall(dt=dt) == INVALID
+
+
+@pytest.mark.parametrize("S,B,H", [(64, 0, 384), (64, 33, 384), (0, 2, 384), (524288, 2, 384),
+                                   (64, 2, 320), (64, 2, 24640), (64, 2, 400)])
+def test_forward_shape_out_of_range(S, B, H):
+    assert fcall(S=S, B=B, H=H) == SHAPE
+
+
+@pytest.mark.parametrize("which", ["x", "w", "y"])
+def test_forward_misaligned_pointer(which):
+    base = {"x": X, "w": W, "y": Y}[which]
+    assert fcall(**{which: base + 8}) == INVALID
+
+
+@pytest.mark.parametrize("case", [dict(y=X), dict(y=X + 2048), dict(y=W - 256), dict(y=M - 512),
+                                  dict(x=Y + 64 * 2 * 384 * 2 - 16)])
+def test_forward_overlapping_buffers(case):
+    assert fcall(**case) == INVALID
 
 
 def test_plan_is_pure_and_consistent():

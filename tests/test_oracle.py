@@ -98,6 +98,22 @@ def pin_hand_cases(orc):
                                        rtol=1e-12, err_msg=tag)
 
 
+FWD_GOLDEN = os.path.join(HERE, "golden", "forward_hand_cases.json")
+
+
+def pin_forward_hand_cases(orc):
+    for c in json.load(open(FWD_GOLDEN))["cases"]:
+        for dtype in ("bf16", "fp16"):
+            x = to_bits(c["x"], dtype)
+            w = to_bits(c["w"], dtype)
+            m = None if c["mask"] is None else np.array(c["mask"], dtype=np.uint8)
+            r = orc.forward16(dtype, x, w, m)
+            exp = np.array(c["y"], dtype=np.float64)
+            tag = f"{c['name']}/{dtype}"
+            assert np.array_equal(r["y64"], exp), (tag, r["y64"], exp)
+            assert np.array_equal(from_bits(r["y16"], dtype), exp), tag
+
+
 def pin_call_example(orc):
     # Call example on the page: S=1, B=2, H=192*2, W=3, FLOAT16, every input (and the bool mask)
     # zero-filled. Whatever the print format, the gradients must be zero.
@@ -282,7 +298,7 @@ def pin_codec_encode_bf16(orc):
     assert np.all(same | zero)
 
 
-PINS = [pin_hand_cases, pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
+PINS = [pin_hand_cases, pin_forward_hand_cases, pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
         pin_codec_decode, pin_codec_roundtrip, pin_codec_encode_fp16, pin_codec_encode_bf16]
 
 
@@ -334,6 +350,10 @@ MUTANTS = [
     ("decoder subnormal scale off", "ldexp((double)f, 1 - bias - pb)", "ldexp((double)f, -bias - pb)"),
     ("decoder bias off by one", "e - bias - pb);", "e - bias - pb + 1);"),
     ("gradWeight rss uses |term|", "sq += term * term;", "sq += fabs(term);"),
+    ("forward taps reversed", "acc += w[k * H + h] * x[", "acc += w[(W - 1 - k) * H + h] * x["),
+    ("forward shifted one row back", "const int64_t src = i - (W - 1) + k;",
+     "const int64_t src = i - W + k;"),
+    ("forward ignores the mask", "y[(i * B + j) * H + h] = m * acc;", "y[(i * B + j) * H + h] = acc;"),
 ]
 
 
