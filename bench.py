@@ -7,6 +7,10 @@ fixed-order gradWeight reduction) over inputs already resident in HBM. Effective
 bytes the method must move: read gradY and x, write gradX (2 bytes each per element), read the mask
 (1 byte per (j,i)), read the weight and write gradWeight; workspace traffic is not counted.
 
+The same run also times the forward (mccb_forward, y = mask * causal conv(x, w)) on the same x,
+weight and mask, reported in the "forward" object of the same line: effective GB/s over its
+algorithmic bytes (read x, write y, read the mask and the weight).
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -30,17 +34,18 @@ def log(msg: str) -> None:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mccb_fused_bwd_S16384_B32_H5120_bf16_traffic.txt")
+FWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mccb_fwd_S16384_B32_H5120_bf16_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "masked_depthwise_causal_amd", "csrc", "mccb.hip")
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter summary, or None if
-    that summary is for another workload or for a different kernel source than the one built."""
+def measured_traffic(workload_name: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per kernel launch from a committed rocprofv3 counter summary, or None if that
+    summary is for another workload or for a different kernel source than the one built."""
     import hashlib
 
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.startswith("#"):
                 k, v = line.strip().split("=", 1)
                 kv[k.strip()] = v.strip()
@@ -113,6 +118,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-forward", action="store_true", help="skip timing the forward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -177,6 +183,30 @@ def main() -> int:
                 "kernel": "mccb_fused_bwd", "avg_ms": round(fused_avg_ms, 5),
                 "reduce_avg_ms": round(reduce_ms / max(n_prof, 1), 5)}
 
+    fwd = None
+    if not args.no_forward:
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            mdc.forward(x, w, m, y=y, stream=stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            mdc.forward(x, w, m, y=y, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        fwd_ms = ev0.elapsed_time(ev1) / args.steps
+        fwd_alg = 4 * wl.N + (wl.B * wl.S if m is not None else 0) + 3 * wl.H * 2
+        fwd_gbs = fwd_alg / (fwd_ms * 1e-3) / 1e9
+        log(f"forward: {fwd_ms:.4f} ms/step, {fwd_gbs:.1f} GB/s")
+        fwd = {"metric": "effective HBM GB/s, masked causal conv1d forward, same workload",
+               "value": round(fwd_gbs, 1), "unit": "GB/s", "ms_per_step": round(fwd_ms, 5),
+               "algorithmic_bytes": fwd_alg,
+               "roofline": {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(wl.name, FWD_TRAFFIC_FILE),
+                            "kernel": "mccb_fwd", "avg_ms": round(fwd_ms, 5)}}
+        del y
+
     ceiling = None
     if not args.no_ceiling:
         ceiling = round(copy_ceiling(torch, dev), 1)
@@ -206,6 +236,7 @@ def main() -> int:
                    "copy_ceiling_gbs": ceiling},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "forward": fwd,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -83,7 +83,7 @@
 #define MCCB_MIN_STRIP_ROWS 128  // ... but not below this many rows per strip
 #endif
 #ifndef MCCB_FWD_VEC
-#define MCCB_FWD_VEC 4  // forward: channels per lane (4 = 8-byte loads)
+#define MCCB_FWD_VEC 8  // forward: channels per lane (8 = 16-byte loads)
 #endif
 #ifndef MCCB_FWD_WAVES
 #define MCCB_FWD_WAVES 8  // forward: wavefronts per block, side by side across the columns
@@ -92,7 +92,7 @@
 #define MCCB_FWD_ROWS 8  // forward: rows one block covers
 #endif
 #ifndef MCCB_FWD_LDS
-#define MCCB_FWD_LDS (82 * 1024)  // forward: LDS reserved per block (more than half a CU's 160 KB)
+#define MCCB_FWD_LDS 0  // forward: LDS reserved per block to cap blocks per CU (0: no cap)
 #endif
 
 namespace {
@@ -480,14 +480,12 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
 // differentiates). Pure streaming: read x, write y, nothing to reduce.
 //
 // A block covers a short tile: kFwdRows rows x kFwdCols contiguous columns (kFwdWaves wavefronts
-// side by side, kFwdVec channels per lane). Tiles are numbered row-major, column tile fastest, so
+// side by side, kFwdVec channels per lane; 8 rows x 4096 columns by default). Tiles are numbered row-major, column tile fastest, so
 // the blocks in flight at any moment sit on a few neighbouring rows; the HBM serves such a compact
-// front markedly faster than many independent column walks. Each block reserves more than half of
-// a CU's LDS (it uses none), so one block runs per CU: fewer, shorter-lived tiles in flight keep
-// the front tighter still. The two rows before the tile are re-read with cached loads (the tile
-// above loaded them, also cached, as its last two rows); the column-tile count is padded to a
-// multiple of the 8 XCDs so that a tile and the tile above it run on the same XCD and share its
-// L2 (padding blocks exit at once).
+// front markedly faster than many independent column walks. The two rows before the tile are
+// re-read with cached loads (the tile above loaded them, also cached, as its last two rows); when
+// the column-tile count is a multiple of the 8 XCDs, which take blocks round-robin, a tile and the
+// tile above it run on the same XCD and the re-read hits its L2.
 //
 // Every output is the exact three-term sum (products of 16-bit values are exact in fp64) rounded
 // once: round-to-odd to fp32, then round-to-nearest-even to the dtype.
@@ -497,7 +495,6 @@ constexpr int kFwdWords = kFwdVec / 2;
 constexpr int kFwdWaves = MCCB_FWD_WAVES;
 constexpr int kFwdRows = MCCB_FWD_ROWS;
 constexpr int kFwdCols = kFwdWaves * kWave * kFwdVec;  // columns of one tile
-constexpr int kXcds = 8;                               // XCDs of an MI355X
 static_assert(kFwdVec == 2 || kFwdVec == 4 || kFwdVec == 8, "forward lane vector: 4, 8 or 16 bytes");
 static_assert(kFwdRows >= 2, "the two look-back rows come from the tile above");
 static_assert(kFwdWaves * kWave <= 1024, "forward block too large");
@@ -519,12 +516,11 @@ template <int DT, bool HAS_MASK>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
-             int64_t H, int64_t n_ct, int64_t n_ct_pad) {
+             int64_t H, int64_t n_ct) {
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
     if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
-    const int64_t ct = blockIdx.x % n_ct_pad;  // column tile (fastest)
-    const int64_t rt = blockIdx.x / n_ct_pad;  // row tile
-    if (ct >= n_ct) return;                    // XCD padding
+    const int64_t ct = blockIdx.x % n_ct;  // column tile (fastest)
+    const int64_t rt = blockIdx.x / n_ct;  // row tile
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t C = B * H;
@@ -689,15 +685,14 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     return e;
 }
 
-// Forward grid: column tiles padded to a multiple of the XCD count, times row tiles.
+// Forward grid: column tiles times row tiles, column tile fastest.
 struct FwdPlan {
-    int64_t n_ct, n_ct_pad, n_rt;
+    int64_t n_ct, n_rt;
 };
 
 FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
     FwdPlan f;
     f.n_ct = (B * H + kFwdCols - 1) / kFwdCols;
-    f.n_ct_pad = (f.n_ct + kXcds - 1) / kXcds * kXcds;
     f.n_rt = (S + kFwdRows - 1) / kFwdRows;
     return f;
 }
@@ -706,15 +701,15 @@ template <int DT>
 hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, const void *x, const void *w,
                       const uint8_t *mask, void *y, hipStream_t st) {
     const FwdPlan f = make_fwd_plan(S, B, H);
-    const dim3 grid((unsigned)(f.n_ct_pad * f.n_rt));
+    const dim3 grid((unsigned)(f.n_ct * f.n_rt));
     const dim3 block(kFwdWaves * kWave);
     if (mask) {
         hipLaunchKernelGGL((mccb_fwd<DT, true>), grid, block, MCCB_FWD_LDS, st, (const fvec_t *)x,
-                           (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, f.n_ct_pad);
+                           (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct);
     } else {
         hipLaunchKernelGGL((mccb_fwd<DT, false>), grid, block, MCCB_FWD_LDS, st,
                            (const fvec_t *)x, (const fvec_t *)w, (const uint8_t *)nullptr,
-                           (fvec_t *)y, S, B, H, f.n_ct, f.n_ct_pad);
+                           (fvec_t *)y, S, B, H, f.n_ct);
     }
     return hipGetLastError();
 }

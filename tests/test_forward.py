@@ -98,8 +98,8 @@ def test_small_workload_full():
 
 
 EDGE = [
-    # (S, B, H, dtype, mask): S around the row tile, B*H around the column tile and the XCD
-    # padding of the column-tile count, every mask kind
+    # (S, B, H, dtype, mask): S around the row tile, B*H below, at and past the column tile
+    # (4096 columns by default), every mask kind
     (1, 2, 384, "bf16", ("bernoulli", 0.8)),
     (2, 1, 384, "fp16", ("null",)),
     (3, 3, 448, "bf16", ("prefix",)),
@@ -114,6 +114,8 @@ EDGE = [
     (5, 32, 24576, "fp16", ("bernoulli", 0.6)),
     (16, 32, 384, "bf16", ("all_false",)),
     (1000, 2, 1024, "bf16", ("bernoulli", 0.9)),
+    (12, 8, 512, "bf16", ("bernoulli", 0.8)),
+    (21, 5, 832, "fp16", ("prefix",)),
 ]
 
 
@@ -159,8 +161,7 @@ def test_null_mask_equals_all_true():
 
 
 def test_output_canaries_untouched():
-    """The kernel writes y and nothing next to it (the column tiles past B*H and the padding
-    blocks exit without a store)."""
+    """The kernel writes y and nothing next to it (lanes past B*H and rows past S store nothing)."""
     wl = custom(19, 3, 448, "fp16", ("bernoulli", 0.8), seed=23)
     x, w, m = (wls.full_tensor(wl, wls.STREAM_X, "cuda"), wls.weight_tensor(wl, "cuda"),
                wls.mask_tensor(wl, "cuda"))
