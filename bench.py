@@ -9,7 +9,8 @@ bytes the method must move: read gradY and x, write gradX (2 bytes each per elem
 
 The same run also times the forward (mccb_forward, y = mask * causal conv(x, w)) on the same x,
 weight and mask, reported in the "forward" object of the same line: effective GB/s over its
-algorithmic bytes (read x, write y, read the mask and the weight).
+algorithmic bytes (read x, write y, read the mask and the weight); and both ops again on the same
+values stored [B,S,H] and passed as strided [S,B,H] views ("strided" object).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -119,6 +120,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-forward", action="store_true", help="skip timing the forward")
+    ap.add_argument("--no-strided", action="store_true",
+                    help="skip timing both ops on [B,S,H]-stored (strided) inputs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,6 +210,42 @@ def main() -> int:
                             "kernel": "mccb_fwd", "avg_ms": round(fwd_ms, 5)}}
         del y
 
+    strided = None
+    if not args.no_strided:
+        # the same values stored [B,S,H] (a batch-major producer), passed as [S,B,H] views: the
+        # kernels read them in place through their strides
+        gy_p = gy.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        x_p = x.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        ws_p = torch.empty(max(1, mdc.mccb_get_workspace_size_ex(
+            gy_p.data_ptr(), x_p.data_ptr(), w.data_ptr(), wl.S, wl.B, wl.H,
+            mdc.DTYPE_CODE[gy.dtype], mdc._strides(gy_p, x_p, w, m))), dtype=torch.uint8,
+            device=dev)
+        y = torch.empty_like(x)
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / args.steps
+
+        b_ms = timed(lambda: mdc.backward(gy_p, x_p, w, m, gradX=gx, gradWeight=gw, workspace=ws_p,
+                                          stream=stream))
+        f_ms = timed(lambda: mdc.forward(x_p, w, m, y=y, stream=stream))
+        f_alg = 4 * wl.N + (wl.B * wl.S if m is not None else 0) + 3 * wl.H * 2
+        strided = {"layout": "gradY and x stored [B,S,H], passed as [S,B,H] views, read in place",
+                   "backward": {"value": round(alg / (b_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "ms_per_step": round(b_ms, 5)},
+                   "forward": {"value": round(f_alg / (f_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "ms_per_step": round(f_ms, 5)}}
+        log(f"strided [B,S,H] inputs: backward {b_ms:.4f} ms, forward {f_ms:.4f} ms")
+        del gy_p, x_p, ws_p, y
+        torch.cuda.empty_cache()
+
     ceiling = None
     if not args.no_ceiling:
         ceiling = round(copy_ceiling(torch, dev), 1)
@@ -237,6 +276,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "forward": fwd,
+        "strided": strided,
     }
     print(json.dumps(out), flush=True)
     return 0

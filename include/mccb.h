@@ -119,6 +119,52 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
 int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
                  int64_t B, int64_t H, int dtype, void *stream);
 
+/*
+ * Strided (non-contiguous) inputs. The parameter table marks gradY, x, weight and mask as
+ * accepting non-contiguous tensors; the outputs gradX, gradWeight (and the forward's y) stay
+ * contiguous. Strides are in elements and >= 0 (0 repeats an element, e.g. a broadcast batch).
+ * Contiguous values: gradY and x {B*H, H, 1}, weight {H, 1}, mask {S, 1}.
+ */
+typedef struct {
+    int64_t gradY[3];  /* along S, B, H */
+    int64_t x[3];      /* along S, B, H */
+    int64_t weight[2]; /* along the tap k, then H */
+    int64_t mask[2];   /* along B, then S */
+} mccb_strides_t;
+
+/*
+ * mccb_backward with strided inputs (strides NULL = all contiguous, same result as
+ * mccb_backward). An input whose channels are contiguous (H stride 1) with even row and batch
+ * strides and a 4-byte aligned base is read in place; any other gradY or x is first packed into a
+ * contiguous copy inside the workspace (one extra read and write of that tensor), and a weight
+ * that is not contiguous and 16-byte aligned is packed too. The mask is read through its strides.
+ * Phase 1 therefore takes the input pointers as well (as the page's phase 1 takes the tensors):
+ * they are inspected for alignment only, never dereferenced. Input bases need 2-byte alignment;
+ * gradX, gradWeight and the workspace stay contiguous and 16-byte aligned. Negative strides, or an
+ * input extent past 2^62 bytes, give MCCB_ERR_PARAM_INVALID; no output or the workspace may
+ * overlap any input's extent. Otherwise as mccb_get_workspace_size / mccb_backward.
+ */
+int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *weight, int64_t S,
+                               int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                               uint64_t *workspace_size);
+int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
+                     const mccb_strides_t *strides, void *workspace, uint64_t workspace_size,
+                     void *stream);
+
+/*
+ * mccb_forward with strided x, weight and mask (strides->gradY is ignored). x is read in place
+ * when its channels are contiguous, its row and batch strides are multiples of 8 and its base is
+ * 16-byte aligned; otherwise it (and a non-contiguous weight) is packed into the workspace,
+ * whose size phase 1 returns (0 when nothing needs packing; the workspace may then be NULL).
+ */
+int mccb_forward_get_workspace_size_ex(const void *x, const void *weight, int64_t S, int64_t B,
+                                       int64_t H, int dtype, const mccb_strides_t *strides,
+                                       uint64_t *workspace_size);
+int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
+                    int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                    void *workspace, uint64_t workspace_size, void *stream);
+
 /* The tiling chosen for a shape, for mccb_backward (first eight fields) and mccb_forward (fwd_*);
  * a pure function of (S, B, H, dtype). Exposed so that tests can place edge cases on tile
  * boundaries. */

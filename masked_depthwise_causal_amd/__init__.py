@@ -15,7 +15,7 @@ import ctypes
 
 import torch
 
-from ._lib import MccbError, Plan, lib, status_string  # noqa: F401
+from ._lib import MccbError, Plan, Strides, lib, status_string  # noqa: F401
 
 MCCB_BF16, MCCB_FP16 = 0, 1
 MCCB_OK = 0
@@ -58,6 +58,47 @@ def mccb_forward(x: int, weight: int, mask: int | None, y: int, S: int, B: int, 
     return int(lib().mccb_forward(x, weight, mask, y, S, B, H, dtype, stream))
 
 
+def mccb_get_workspace_size_ex(gradY: int, x: int, weight: int, S: int, B: int, H: int, dtype: int,
+                               strides: Strides | None) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib().mccb_get_workspace_size_ex(gradY, x, weight, S, B, H, dtype,
+                                          None if strides is None else ctypes.byref(strides),
+                                          ctypes.byref(out))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_get_workspace_size_ex")
+    return int(out.value)
+
+
+def mccb_backward_ex(gradY: int, x: int, weight: int, mask: int | None, gradX: int,
+                     gradWeight: int, S: int, B: int, H: int, dtype: int,
+                     strides: Strides | None, workspace: int | None, workspace_size: int,
+                     stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_backward_ex(gradY, x, weight, mask, gradX, gradWeight, S, B, H, dtype,
+                                      None if strides is None else ctypes.byref(strides),
+                                      workspace, workspace_size, stream))
+
+
+def mccb_forward_get_workspace_size_ex(x: int, weight: int, S: int, B: int, H: int, dtype: int,
+                                       strides: Strides | None) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib().mccb_forward_get_workspace_size_ex(
+        x, weight, S, B, H, dtype, None if strides is None else ctypes.byref(strides),
+        ctypes.byref(out))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_forward_get_workspace_size_ex")
+    return int(out.value)
+
+
+def mccb_forward_ex(x: int, weight: int, mask: int | None, y: int, S: int, B: int, H: int,
+                    dtype: int, strides: Strides | None, workspace: int | None,
+                    workspace_size: int, stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_forward_ex(x, weight, mask, y, S, B, H, dtype,
+                                     None if strides is None else ctypes.byref(strides),
+                                     workspace, workspace_size, stream))
+
+
 def mccb_status_string(status: int) -> str:
     return status_string(status)
 
@@ -78,7 +119,7 @@ def mccb_profile_end() -> tuple[float, float, int]:
 
 
 # -- tensor front end ---------------------------------------------------------------------------------
-def _check_tensor(name, t, shape, dtype, device):
+def _check_tensor(name, t, shape, dtype, device, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device or t.device.type != "cuda":
@@ -87,8 +128,27 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if not contiguous and any(st < 0 for st in t.stride()):
+        raise ValueError(f"{name} has a negative stride")
+
+
+def _strides(gradY, x, weight, mask) -> Strides | None:
+    """mccb_strides_t of the inputs, or None when every input is contiguous."""
+    ts = [t for t in (gradY, x, weight, mask) if t is not None]
+    if all(t.is_contiguous() for t in ts):
+        return None
+    st = Strides()
+    if gradY is not None:
+        st.gradY[:] = list(gradY.stride())
+    else:
+        st.gradY[:] = list(x.stride())
+    st.x[:] = list(x.stride())
+    st.weight[:] = list(weight.stride())
+    S, B = int(x.shape[0]), int(x.shape[1])
+    st.mask[:] = list(mask.stride()) if mask is not None else [S, 1]
+    return st
 
 
 def workspace_for(S: int, B: int, H: int, dtype: torch.dtype, device) -> torch.Tensor:
@@ -100,9 +160,10 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
              mask: torch.Tensor | None = None, gradX: torch.Tensor | None = None,
              gradWeight: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
              stream: torch.cuda.Stream | None = None):
-    """gradX [S,B,H], gradWeight [3,H] for contiguous device tensors (outputs allocated if None).
+    """gradX [S,B,H], gradWeight [3,H] on device tensors (outputs allocated if None).
 
-    Enqueues on `stream` (default: torch's current stream) and returns without synchronizing.
+    The inputs may be strided views (mccb_backward_ex); the outputs must be contiguous. Enqueues
+    on `stream` (default: torch's current stream) and returns without synchronizing.
     """
     if gradY.dim() != 3:
         raise ValueError("gradY must be [S,B,H]")
@@ -111,54 +172,80 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     dt = gradY.dtype
     if dt not in DTYPE_CODE:
         raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
-    _check_tensor("gradY", gradY, (S, B, H), dt, dev)
-    _check_tensor("x", x, (S, B, H), dt, dev)
-    _check_tensor("weight", weight, (3, H), dt, dev)
+    _check_tensor("gradY", gradY, (S, B, H), dt, dev, contiguous=False)
+    _check_tensor("x", x, (S, B, H), dt, dev, contiguous=False)
+    _check_tensor("weight", weight, (3, H), dt, dev, contiguous=False)
     if mask is not None:
-        _check_tensor("mask", mask, (B, S), None, dev)
+        _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
             raise ValueError("mask must be bool or uint8")
     if gradX is None:
-        gradX = torch.empty_like(gradY)
+        gradX = torch.empty((S, B, H), dtype=dt, device=dev)
     if gradWeight is None:
-        gradWeight = torch.empty_like(weight)
+        gradWeight = torch.empty((3, H), dtype=dt, device=dev)
     _check_tensor("gradX", gradX, (S, B, H), dt, dev)
     _check_tensor("gradWeight", gradWeight, (3, H), dt, dev)
-    if workspace is None:
-        workspace = workspace_for(S, B, H, dt, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
-                       None if mask is None else mask.data_ptr(), gradX.data_ptr(),
-                       gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt], workspace.data_ptr(),
-                       workspace.numel(), st.cuda_stream)
+    strides = _strides(gradY, x, weight, mask)
+    mptr = None if mask is None else mask.data_ptr()
+    if strides is None:
+        if workspace is None:
+            workspace = workspace_for(S, B, H, dt, dev)
+        rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
+                           gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt],
+                           workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+        where = "mccb_backward"
+    else:
+        if workspace is None:
+            n = mccb_get_workspace_size_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), S, B,
+                                           H, DTYPE_CODE[dt], strides)
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        rc = mccb_backward_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
+                              gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt],
+                              strides, workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+        where = "mccb_backward_ex"
     if rc != MCCB_OK:
-        raise MccbError(rc, "mccb_backward")
+        raise MccbError(rc, where)
     return gradX, gradWeight
 
 
 def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = None,
-            y: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """y [S,B,H] = mask * causal depthwise conv(x, weight) for contiguous device tensors (y
-    allocated if None). Enqueues on `stream` (default: torch's current stream) without
-    synchronizing."""
+            y: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [S,B,H] = mask * causal depthwise conv(x, weight) on device tensors (y allocated if
+    None). The inputs may be strided views (mccb_forward_ex); y must be contiguous. Enqueues on
+    `stream` (default: torch's current stream) without synchronizing."""
     if x.dim() != 3:
         raise ValueError("x must be [S,B,H]")
     S, B, H = (int(s) for s in x.shape)
     dev, dt = x.device, x.dtype
     if dt not in DTYPE_CODE:
         raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
-    _check_tensor("x", x, (S, B, H), dt, dev)
-    _check_tensor("weight", weight, (3, H), dt, dev)
+    _check_tensor("x", x, (S, B, H), dt, dev, contiguous=False)
+    _check_tensor("weight", weight, (3, H), dt, dev, contiguous=False)
     if mask is not None:
-        _check_tensor("mask", mask, (B, S), None, dev)
+        _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
             raise ValueError("mask must be bool or uint8")
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty((S, B, H), dtype=dt, device=dev)
     _check_tensor("y", y, (S, B, H), dt, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    rc = mccb_forward(x.data_ptr(), weight.data_ptr(), None if mask is None else mask.data_ptr(),
-                      y.data_ptr(), S, B, H, DTYPE_CODE[dt], st.cuda_stream)
+    strides = _strides(None, x, weight, mask)
+    mptr = None if mask is None else mask.data_ptr()
+    if strides is None:
+        rc = mccb_forward(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H,
+                          DTYPE_CODE[dt], st.cuda_stream)
+        where = "mccb_forward"
+    else:
+        if workspace is None:
+            n = mccb_forward_get_workspace_size_ex(x.data_ptr(), weight.data_ptr(), S, B, H,
+                                                   DTYPE_CODE[dt], strides)
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        rc = mccb_forward_ex(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H,
+                             DTYPE_CODE[dt], strides, workspace.data_ptr(), workspace.numel(),
+                             st.cuda_stream)
+        where = "mccb_forward_ex"
     if rc != MCCB_OK:
-        raise MccbError(rc, "mccb_forward")
+        raise MccbError(rc, where)
     return y

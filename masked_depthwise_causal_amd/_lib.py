@@ -25,6 +25,12 @@ class Plan(ctypes.Structure):
                 ("fwd_n_col_tiles", ctypes.c_int64), ("fwd_n_row_tiles", ctypes.c_int64)]
 
 
+class Strides(ctypes.Structure):
+    """mccb_strides_t: element strides of gradY / x (S, B, H), weight (k, H), mask (B, S)."""
+    _fields_ = [("gradY", ctypes.c_int64 * 3), ("x", ctypes.c_int64 * 3),
+                ("weight", ctypes.c_int64 * 2), ("mask", ctypes.c_int64 * 2)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library, building it first if no build exists."""
     global _lib
@@ -42,6 +48,18 @@ def lib() -> ctypes.CDLL:
         L.mccb_backward.restype = ctypes.c_int
         L.mccb_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
         L.mccb_forward.restype = ctypes.c_int
+        sp = ctypes.POINTER(Strides)
+        L.mccb_get_workspace_size_ex.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, sp,
+                                                 ctypes.POINTER(u64)]
+        L.mccb_get_workspace_size_ex.restype = ctypes.c_int
+        L.mccb_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, sp,
+                                       vp, u64, vp]
+        L.mccb_backward_ex.restype = ctypes.c_int
+        L.mccb_forward_get_workspace_size_ex.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, sp,
+                                                         ctypes.POINTER(u64)]
+        L.mccb_forward_get_workspace_size_ex.restype = ctypes.c_int
+        L.mccb_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, sp, vp, u64, vp]
+        L.mccb_forward_ex.restype = ctypes.c_int
         L.mccb_status_string.argtypes = [ctypes.c_int]
         L.mccb_status_string.restype = ctypes.c_char_p
         L.mccb_profile_begin.argtypes = [ctypes.c_int]

@@ -240,13 +240,26 @@ __device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
 // Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + 2) mask bytes.
 // Workspace: fp64 partials [n_strips][3][C].
 // ---------------------------------------------------------------------------------------------
-template <int DT, bool HAS_MASK>
+// Input strides (in elements; channels contiguous, so only the row and batch strides vary): a
+// contiguous [S,B,H] tensor has row stride B*H and batch stride H. With STRIDED false the kernel
+// assumes that layout for gradY and x; with STRIDED true it takes each tensor's own strides. Either
+// way a load address is a wave-uniform 64-bit base (row, and for STRIDED the block's first batch)
+// plus a 32-bit lane offset; the host reads an input in place only when that offset fits (a block
+// spans at most three batches). The mask is always addressed through its strides (batch, row),
+// which cost nothing in the once-per-strip staging loop.
+struct InStrides {
+    int64_t gy_row, gy_batch, x_row, x_batch, m_batch, m_row;
+};
+
+// The strided variant keeps a second lane offset and row stride; it is compiled for one wavefront
+// less per SIMD so that it does not spill.
+template <int DT, bool HAS_MASK, bool STRIDED>
 __global__ void __launch_bounds__(kBlockWaves *kWave)
-    __attribute__((amdgpu_waves_per_eu(MCCB_WAVES_PER_SIMD)))
+    __attribute__((amdgpu_waves_per_eu(STRIDED ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD)))
     mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
                    const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
                    vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
-                   int64_t rows_per_strip, int64_t n_col_blocks) {
+                   int64_t rows_per_strip, int64_t n_col_blocks, InStrides st) {
     extern __shared__ uint8_t smask[];
     __shared__ f64x2 red[kBlockWaves][kWave * kVec / 2];
 
@@ -281,7 +294,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
         for (int t = threadIdx.x; t < nj * span; t += blockDim.x) {
             const int jj = t / span;
             const int64_t row = rs0 + (t - jj * span);
-            smask[t] = (row < S) ? mask[(j_first + jj) * S + row] : (uint8_t)0;
+            smask[t] = (row < S) ? mask[(j_first + jj) * st.m_batch + row * st.m_row] : (uint8_t)0;
         }
         moff = (int)(j - j_first) * span;
         __syncthreads();
@@ -318,9 +331,19 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
     const int64_t row_bytes = C * 2;
     const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
-    auto at = [&](const vec_t *base, int64_t row) -> const vec_t * {
-        return reinterpret_cast<const vec_t *>(reinterpret_cast<const char *>(base) +
-                                               row * row_bytes + lane_off);
+    // STRIDED: the block's first batch goes into the uniform base, the lane keeps the rest
+    const int64_t jb = (col_block * kBlockCols) / H;
+    const char *gy_base = reinterpret_cast<const char *>(gy) + (STRIDED ? jb * st.gy_batch * 2 : 0);
+    const char *x_base = reinterpret_cast<const char *>(x) + (STRIDED ? jb * st.x_batch * 2 : 0);
+    const int64_t gy_rb = STRIDED ? st.gy_row * 2 : row_bytes;
+    const int64_t x_rb = STRIDED ? st.x_row * 2 : row_bytes;
+    const uint32_t gy_lane = STRIDED ? (uint32_t)(((j - jb) * st.gy_batch + h) * 2) : lane_off;
+    const uint32_t x_lane = STRIDED ? (uint32_t)(((j - jb) * st.x_batch + h) * 2) : lane_off;
+    auto at_gy = [&](int64_t row) -> const vec_t * {
+        return reinterpret_cast<const vec_t *>(gy_base + row * gy_rb + gy_lane);
+    };
+    auto at_x = [&](int64_t row) -> const vec_t * {
+        return reinterpret_cast<const vec_t *>(x_base + row * x_rb + x_lane);
     };
     auto out_at = [&](int64_t row) -> vec_t * {
         return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx) + row * row_bytes + lane_off);
@@ -336,13 +359,13 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     // last two are the next wave's first: cached loads, so those come from L2; the rest stream.
     auto issue = [&](int64_t r0, vec_t (&qy)[kTurnRows + 2], vec_t (&qx)[kTurnRows]) {
         const int64_t i0 = r0 + ring * kTurnRows;
-        qy[0] = load_vec_cached(at(gy, i0));
-        qy[1] = load_vec_cached(at(gy, i0 + 1));
+        qy[0] = load_vec_cached(at_gy(i0));
+        qy[1] = load_vec_cached(at_gy(i0 + 1));
 #pragma unroll
         for (int u = 0; u < kTurnRows; ++u) {
-            qy[u + 2] = (u + 2 >= kTurnRows) ? load_vec_cached(at(gy, i0 + 2 + u))
-                                             : load_vec(at(gy, i0 + 2 + u));
-            qx[u] = load_vec(at(x, i0 + u));
+            qy[u + 2] = (u + 2 >= kTurnRows) ? load_vec_cached(at_gy(i0 + 2 + u))
+                                             : load_vec(at_gy(i0 + 2 + u));
+            qx[u] = load_vec(at_x(i0 + u));
         }
     };
     auto compute = [&](int64_t r0, const vec_t (&qy)[kTurnRows + 2], const vec_t (&qx)[kTurnRows]) {
@@ -369,11 +392,11 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
         if (i0 >= rs1) return;
         const int64_t i1 = (i0 + kTurnRows < rs1) ? i0 + kTurnRows : rs1;
         double d0[kVec], d1[kVec], d2[kVec];
-        widen<DT>((i0 < S && keep(i0)) ? load_vec_cached(at(gy, i0)) : zero, d0);
-        widen<DT>((i0 + 1 < S && keep(i0 + 1)) ? load_vec_cached(at(gy, i0 + 1)) : zero, d1);
+        widen<DT>((i0 < S && keep(i0)) ? load_vec_cached(at_gy(i0)) : zero, d0);
+        widen<DT>((i0 + 1 < S && keep(i0 + 1)) ? load_vec_cached(at_gy(i0 + 1)) : zero, d1);
         for (int64_t i = i0; i < i1; ++i) {
-            widen<DT>((i + 2 < S && keep(i + 2)) ? load_vec_cached(at(gy, i + 2)) : zero, d2);
-            const vec_t r = stencil_row<DT>(d0, d1, d2, load_vec(at(x, i)), w0, w1, w2, a0, a1, a2);
+            widen<DT>((i + 2 < S && keep(i + 2)) ? load_vec_cached(at_gy(i + 2)) : zero, d2);
+            const vec_t r = stencil_row<DT>(d0, d1, d2, load_vec(at_x(i)), w0, w1, w2, a0, a1, a2);
             if (active) store_vec(out_at(i), r);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
@@ -512,11 +535,11 @@ __device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
     }
 }
 
-template <int DT, bool HAS_MASK>
+template <int DT, bool HAS_MASK, bool STRIDED>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
-             int64_t H, int64_t n_ct) {
+             int64_t H, int64_t n_ct, InStrides st) {
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
     if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
     const int64_t ct = blockIdx.x % n_ct;  // column tile (fastest)
@@ -539,7 +562,10 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
         const int64_t row = r0 - 2 + u;
         fvec_t q = {};
         if (row >= 0 && row < S) {
-            const fvec_t *p = x + row * CV + v;
+            const fvec_t *p = STRIDED ? reinterpret_cast<const fvec_t *>(
+                                            reinterpret_cast<const char *>(x) +
+                                            (row * st.x_row + j * st.x_batch + h0) * 2)
+                                      : x + row * CV + v;
             q = (u < 2 || u >= kFwdRows) ? *p : __builtin_nontemporal_load(p);
         }
         xr[u] = q;
@@ -552,9 +578,9 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
 #pragma unroll
     for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
     if (HAS_MASK) {
-        const uint8_t *mrow = mask + j * S + r0;
+        const uint8_t *mrow = mask + j * st.m_batch + r0 * st.m_row;
 #pragma unroll
-        for (int u = 0; u < kFwdRows; ++u) keep[u] = (r0 + u < S) ? mrow[u] : 0;
+        for (int u = 0; u < kFwdRows; ++u) keep[u] = (r0 + u < S) ? mrow[u * st.m_row] : 0;
     }
 
     double a[kFwdVec], b[kFwdVec], c[kFwdVec];
@@ -582,6 +608,25 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
             a[e] = b[e];
             b[e] = c[e];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Pack kernel: gathers a strided 16-bit [R0, R1, H] tensor into contiguous rows of the workspace,
+// dst[(a*R1 + b)*H + h] = src[a*s0 + b*s1 + h*s2], for inputs the kernels above cannot read in
+// place (channels not contiguous, or rows misaligned for their vector loads). One block per
+// (a, b) row; each lane writes two channels as one 32-bit store (H is even).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+    mccb_pack(const uint16_t *__restrict__ src, uint32_t *__restrict__ dst, int64_t R1, int64_t H,
+              int64_t s0, int64_t s1, int64_t s2) {
+    const int64_t r = blockIdx.x;
+    const int64_t a = r / R1, b = r - a * R1;
+    const uint16_t *row = src + a * s0 + b * s1;
+    uint32_t *out = dst + r * (H / 2);
+    for (int64_t q = threadIdx.x; q < H / 2; q += blockDim.x) {
+        const uint32_t lo = row[(2 * q) * s2], hi = row[(2 * q + 1) * s2];
+        out[q] = lo | (hi << 16);
     }
 }
 
@@ -656,23 +701,23 @@ struct Profile {
 
 template <int DT>
 hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, const uint8_t *mask,
-                  void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev) {
+                  void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev,
+                  const InStrides &is, bool strided) {
     const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
     const dim3 block1(kBlockWaves * kWave);
     const size_t lds_floor = MCCB_LDS_FLOOR;
+    const size_t lds = mask ? (p.mask_lds > lds_floor ? p.mask_lds : lds_floor) : lds_floor;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
+#define MCCB_FUSED(M, T)                                                                          \
+    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T>), grid1, block1, lds, st, (const vec_t *)gy,     \
+                       (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx, (double *)ws, p.S,  \
+                       p.B, p.H, p.rows_per_strip, p.n_col_blocks, is)
     if (mask) {
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, true>), grid1, block1,
-                           p.mask_lds > lds_floor ? p.mask_lds : lds_floor, st,
-                           (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask,
-                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
-                           p.n_col_blocks);
+        if (strided) MCCB_FUSED(true, true); else MCCB_FUSED(true, false);
     } else {
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, false>), grid1, block1, lds_floor, st, (const vec_t *)gy,
-                           (const vec_t *)x, (const vec_t *)w, (const uint8_t *)nullptr,
-                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip,
-                           p.n_col_blocks);
+        if (strided) MCCB_FUSED(false, true); else MCCB_FUSED(false, false);
     }
+#undef MCCB_FUSED
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hipErrorInvalidValue;
@@ -699,19 +744,140 @@ FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
 
 template <int DT>
 hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, const void *x, const void *w,
-                      const uint8_t *mask, void *y, hipStream_t st) {
+                      const uint8_t *mask, void *y, hipStream_t st, const InStrides &is,
+                      bool strided) {
     const FwdPlan f = make_fwd_plan(S, B, H);
     const dim3 grid((unsigned)(f.n_ct * f.n_rt));
     const dim3 block(kFwdWaves * kWave);
+#define MCCB_FWD(M, T)                                                                            \
+    hipLaunchKernelGGL((mccb_fwd<DT, M, T>), grid, block, MCCB_FWD_LDS, st, (const fvec_t *)x,     \
+                       (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, is)
     if (mask) {
-        hipLaunchKernelGGL((mccb_fwd<DT, true>), grid, block, MCCB_FWD_LDS, st, (const fvec_t *)x,
-                           (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct);
+        if (strided) MCCB_FWD(true, true); else MCCB_FWD(true, false);
     } else {
-        hipLaunchKernelGGL((mccb_fwd<DT, false>), grid, block, MCCB_FWD_LDS, st,
-                           (const fvec_t *)x, (const fvec_t *)w, (const uint8_t *)nullptr,
-                           (fvec_t *)y, S, B, H, f.n_ct);
+        if (strided) MCCB_FWD(false, true); else MCCB_FWD(false, false);
     }
+#undef MCCB_FWD
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Strided inputs. A 3-D input is read in place when its channels are contiguous and its row and
+// batch strides and base keep every lane's vector load aligned; otherwise it is first packed into
+// a contiguous copy in the workspace (after the gradWeight partials, 256-byte aligned). A
+// non-contiguous weight is always packed (3*H elements). The mask is always read in place.
+// ---------------------------------------------------------------------------------------------
+struct View3 {
+    const void *p;
+    int64_t s0, s1, s2;  // element strides along S, B, H
+};
+
+// `span_limit`: if > 0, the lane-relative byte offset ((batches a block spans - 1) * batch
+// stride + H) * 2 must stay below it (the backward kernel keeps it in 32 bits).
+bool inplace3(const View3 &v, int vec, int64_t H, uint64_t span_limit) {
+    if (!(v.s2 == 1 && v.s0 % vec == 0 && v.s1 % vec == 0 &&
+          ((uintptr_t)v.p % (uintptr_t)(vec * 2)) == 0))
+        return false;
+    if (span_limit == 0) return true;
+    const int64_t extra_batches = (kBlockCols - 1) / H + 1;  // j - (block's first batch), at most
+    const unsigned __int128 rel = ((unsigned __int128)extra_batches * (uint64_t)v.s1 + (uint64_t)H) * 2u;
+    return rel < span_limit;
+}
+
+// Bytes from the base to one past the last element, or 0 if that does not fit in 2^62.
+uint64_t extent_bytes(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2,
+                      int64_t esz) {
+    unsigned __int128 last = (unsigned __int128)(n0 - 1) * (uint64_t)s0 +
+                             (unsigned __int128)(n1 - 1) * (uint64_t)s1 +
+                             (unsigned __int128)(n2 - 1) * (uint64_t)s2;
+    unsigned __int128 bytes = (last + 1) * (uint64_t)esz;
+    return bytes >> 62 ? 0 : (uint64_t)bytes;
+}
+
+uint64_t align256(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+constexpr uint64_t kLaneSpan = (uint64_t)1 << 32;  // backward lane offsets are 32-bit
+
+struct ExLayout {
+    bool pack_gy = false, pack_x = false, pack_w = false;
+    uint64_t gy_off = 0, x_off = 0, w_off = 0, total = 0;
+};
+
+// Workspace layout: `base` bytes of the kernels' own scratch, then the packed copies needed.
+ExLayout ex_layout(uint64_t base, int64_t S, int64_t B, int64_t H, const View3 *gy, const View3 &x,
+                   const void *w, int64_t w0, int64_t w1, int vec, uint64_t span_limit) {
+    ExLayout L;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u;
+    uint64_t off = base;
+    if (gy && !inplace3(*gy, vec, H, span_limit)) {
+        L.pack_gy = true;
+        L.gy_off = off = align256(off);
+        off += nb;
+    }
+    if (!inplace3(x, vec, H, span_limit)) {
+        L.pack_x = true;
+        L.x_off = off = align256(off);
+        off += nb;
+    }
+    if (!(w0 == H && w1 == 1 && ((uintptr_t)w & 15u) == 0)) {
+        L.pack_w = true;
+        L.w_off = off = align256(off);
+        off += (uint64_t)(3 * H) * 2u;
+    }
+    L.total = off;
+    return L;
+}
+
+hipError_t pack3(const void *src, void *dst, int64_t R0, int64_t R1, int64_t H, int64_t s0,
+                 int64_t s1, int64_t s2, hipStream_t st) {
+    hipLaunchKernelGGL(mccb_pack, dim3((unsigned)(R0 * R1)), dim3(256), 0, st,
+                       (const uint16_t *)src, (uint32_t *)dst, R1, H, s0, s1, s2);
+    return hipGetLastError();
+}
+
+// Validated strided arguments shared by the _ex entry points.
+struct ExArgs {
+    View3 gy{}, x{};
+    int64_t w0 = 0, w1 = 0, m0 = 0, m1 = 0;  // weight (tap, H) and mask (B, S) strides
+    uint64_t gy_ext = 0, x_ext = 0, w_ext = 0, m_ext = 0;
+};
+
+// Fills `a` from the strides (NULL = contiguous) and checks them: non-negative, element-aligned
+// bases, extents that fit. `gy` may be NULL (forward).
+int check_strided(const void *gy, const void *x, const void *w, const uint8_t *mask, int64_t S,
+                  int64_t B, int64_t H, const mccb_strides_t *sp, ExArgs &a) {
+    const int64_t C = B * H;
+    a.gy = View3{gy, C, H, 1};
+    a.x = View3{x, C, H, 1};
+    a.w0 = H, a.w1 = 1, a.m0 = S, a.m1 = 1;
+    if (sp) {
+        a.gy = View3{gy, sp->gradY[0], sp->gradY[1], sp->gradY[2]};
+        a.x = View3{x, sp->x[0], sp->x[1], sp->x[2]};
+        a.w0 = sp->weight[0], a.w1 = sp->weight[1], a.m0 = sp->mask[0], a.m1 = sp->mask[1];
+    }
+    const int64_t all[10] = {a.gy.s0, a.gy.s1, a.gy.s2, a.x.s0, a.x.s1, a.x.s2, a.w0, a.w1, a.m0, a.m1};
+    for (int64_t v : all)
+        if (v < 0) return MCCB_ERR_PARAM_INVALID;
+    if ((gy && ((uintptr_t)gy & 1u)) || ((uintptr_t)x & 1u) || ((uintptr_t)w & 1u))
+        return MCCB_ERR_PARAM_INVALID;
+    a.gy_ext = gy ? extent_bytes(S, a.gy.s0, B, a.gy.s1, H, a.gy.s2, 2) : 0;
+    a.x_ext = extent_bytes(S, a.x.s0, B, a.x.s1, H, a.x.s2, 2);
+    a.w_ext = extent_bytes(3, a.w0, 1, 0, H, a.w1, 2);
+    a.m_ext = mask ? extent_bytes(B, a.m0, S, a.m1, 1, 0, 1) : 0;
+    if ((gy && !a.gy_ext) || !a.x_ext || !a.w_ext || (mask && !a.m_ext)) return MCCB_ERR_PARAM_INVALID;
+    return MCCB_OK;
+}
+
+// No output (nor the workspace) may overlap another buffer.
+bool any_overlap(const void *const *bufs, const uint64_t *lens, int n, int first_output) {
+    for (int o = first_output; o < n; ++o) {
+        if (!bufs[o] || lens[o] == 0) continue;
+        for (int t = 0; t < n; ++t) {
+            if (t == o || !bufs[t] || lens[t] == 0) continue;
+            if (overlaps(bufs[o], lens[o], bufs[t], lens[t])) return true;
+        }
+    }
+    return false;
 }
 
 }  // namespace
@@ -781,8 +947,10 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
     }
     const hipError_t e =
         (dtype == MCCB_BF16)
-            ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev)
-            : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev);
+            ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
+                                InStrides{B * H, H, B * H, H, S, 1}, false)
+            : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
+                                InStrides{B * H, H, B * H, H, S, 1}, false);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 
@@ -798,9 +966,134 @@ int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y
     if (overlaps(y, nb, x, nb) || overlaps(y, nb, weight, wb) || (mask && overlaps(y, nb, mask, mb)))
         return MCCB_ERR_PARAM_INVALID;
     hipStream_t st = (hipStream_t)stream;
+    const InStrides is{B * H, H, B * H, H, S, 1};
     const hipError_t e = (dtype == MCCB_BF16)
-                             ? launch_fwd<MCCB_BF16>(S, B, H, x, weight, mask, y, st)
-                             : launch_fwd<MCCB_FP16>(S, B, H, x, weight, mask, y, st);
+                             ? launch_fwd<MCCB_BF16>(S, B, H, x, weight, mask, y, st, is, false)
+                             : launch_fwd<MCCB_FP16>(S, B, H, x, weight, mask, y, st, is, false);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *weight, int64_t S,
+                               int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                               uint64_t *workspace_size) {
+    if (!gradY || !x || !weight || !workspace_size) return MCCB_ERR_PARAM_NULLPTR;
+    int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    ExArgs a;
+    rc = check_strided(gradY, x, weight, nullptr, S, B, H, strides, a);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(S, B, H, dtype);
+    *workspace_size = ex_layout(p.ws_bytes, S, B, H, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan).total;
+    return MCCB_OK;
+}
+
+int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
+                     const mccb_strides_t *strides, void *workspace, uint64_t workspace_size,
+                     void *stream) {
+    if (!gradY || !x || !weight || !gradX || !gradWeight) return MCCB_ERR_PARAM_NULLPTR;
+    int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    ExArgs a;
+    rc = check_strided(gradY, x, weight, mask, S, B, H, strides, a);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(S, B, H, dtype);
+    const ExLayout L = ex_layout(p.ws_bytes, S, B, H, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan);
+    if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
+    if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
+    if (!aligned16(gradX) || !aligned16(gradWeight) || (L.total > 0 && !aligned16(workspace)))
+        return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
+    const void *bufs[7] = {gradY, x, weight, mask, gradX, gradWeight, workspace};
+    const uint64_t lens[7] = {a.gy_ext, a.x_ext, a.w_ext, a.m_ext, nb, wb, L.total};
+    if (any_overlap(bufs, lens, 7, 4)) return MCCB_ERR_PARAM_INVALID;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *wsb = (char *)workspace;
+    const int64_t C = B * H;
+    const void *gy_eff = gradY, *x_eff = x, *w_eff = weight;
+    InStrides is{a.gy.s0, a.gy.s1, a.x.s0, a.x.s1, a.m0, a.m1};
+    if (L.pack_gy) {
+        if (pack3(gradY, wsb + L.gy_off, S, B, H, a.gy.s0, a.gy.s1, a.gy.s2, st) != hipSuccess)
+            return MCCB_ERR_RUNTIME;
+        gy_eff = wsb + L.gy_off, is.gy_row = C, is.gy_batch = H;
+    }
+    if (L.pack_x) {
+        if (pack3(x, wsb + L.x_off, S, B, H, a.x.s0, a.x.s1, a.x.s2, st) != hipSuccess)
+            return MCCB_ERR_RUNTIME;
+        x_eff = wsb + L.x_off, is.x_row = C, is.x_batch = H;
+    }
+    if (L.pack_w) {
+        if (pack3(weight, wsb + L.w_off, 3, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
+            return MCCB_ERR_RUNTIME;
+        w_eff = wsb + L.w_off;
+    }
+    const bool strided = !(is.gy_row == C && is.gy_batch == H && is.x_row == C && is.x_batch == H);
+    hipEvent_t *ev = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.on && g_prof.n < g_prof.cap) ev = &g_prof.ev[3 * (size_t)g_prof.n++];
+    }
+    const hipError_t e =
+        (dtype == MCCB_BF16)
+            ? launch<MCCB_BF16>(p, gy_eff, x_eff, w_eff, mask, gradX, gradWeight, workspace, st, ev,
+                                is, strided)
+            : launch<MCCB_FP16>(p, gy_eff, x_eff, w_eff, mask, gradX, gradWeight, workspace, st, ev,
+                                is, strided);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+int mccb_forward_get_workspace_size_ex(const void *x, const void *weight, int64_t S, int64_t B,
+                                       int64_t H, int dtype, const mccb_strides_t *strides,
+                                       uint64_t *workspace_size) {
+    if (!x || !weight || !workspace_size) return MCCB_ERR_PARAM_NULLPTR;
+    int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    ExArgs a;
+    rc = check_strided(nullptr, x, weight, nullptr, S, B, H, strides, a);
+    if (rc != MCCB_OK) return rc;
+    *workspace_size = ex_layout(0, S, B, H, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0).total;
+    return MCCB_OK;
+}
+
+int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
+                    int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                    void *workspace, uint64_t workspace_size, void *stream) {
+    if (!x || !weight || !y) return MCCB_ERR_PARAM_NULLPTR;
+    int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    ExArgs a;
+    rc = check_strided(nullptr, x, weight, mask, S, B, H, strides, a);
+    if (rc != MCCB_OK) return rc;
+    const ExLayout L = ex_layout(0, S, B, H, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0);
+    if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
+    if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
+    if (!aligned16(y) || (L.total > 0 && !aligned16(workspace))) return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u;
+    const void *bufs[5] = {x, weight, mask, y, L.total ? workspace : nullptr};
+    const uint64_t lens[5] = {a.x_ext, a.w_ext, a.m_ext, nb, L.total};
+    if (any_overlap(bufs, lens, 5, 3)) return MCCB_ERR_PARAM_INVALID;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *wsb = (char *)workspace;
+    const int64_t C = B * H;
+    const void *x_eff = x, *w_eff = weight;
+    InStrides is{C, H, a.x.s0, a.x.s1, a.m0, a.m1};
+    if (L.pack_x) {
+        if (pack3(x, wsb + L.x_off, S, B, H, a.x.s0, a.x.s1, a.x.s2, st) != hipSuccess)
+            return MCCB_ERR_RUNTIME;
+        x_eff = wsb + L.x_off, is.x_row = C, is.x_batch = H;
+    }
+    if (L.pack_w) {
+        if (pack3(weight, wsb + L.w_off, 3, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
+            return MCCB_ERR_RUNTIME;
+        w_eff = wsb + L.w_off;
+    }
+    const bool strided = !(is.x_row == C && is.x_batch == H);
+    const hipError_t e =
+        (dtype == MCCB_BF16)
+            ? launch_fwd<MCCB_BF16>(S, B, H, x_eff, w_eff, mask, y, st, is, strided)
+            : launch_fwd<MCCB_FP16>(S, B, H, x_eff, w_eff, mask, y, st, is, strided);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 

@@ -196,3 +196,106 @@ def test_python_binding_raises_on_bad_shape():
     with pytest.raises(mdc.MccbError) as e:
         mdc.mccb_get_workspace_size(64, 2, 100, BF16)
     assert e.value.status == SHAPE
+
+
+# -- strided inputs (mccb_*_ex) ------------------------------------------------------------------
+def strides(S=64, B=2, H=384, gy=None, x=None, w=None, m=None):
+    st = mdc.Strides()
+    st.gradY[:] = gy or [B * H, H, 1]
+    st.x[:] = x or [B * H, H, 1]
+    st.weight[:] = w or [H, 1]
+    st.mask[:] = m or [S, 1]
+    return st
+
+
+def xcall(gy=GY, x=X, w=W, m=M, gx=GX, gw=GW, S=64, B=2, H=384, dt=BF16, st=None, ws=WS,
+          wsz=1 << 40):
+    rc = mdc.mccb_backward_ex(gy, x, w, m, gx, gw, S, B, H, dt, st, ws, wsz, None)
+    assert rc in VALIDATION_CODES, f"strided call passed validation with fake pointers (rc={rc})"
+    return rc
+
+
+def test_ex_null_strides_is_the_contiguous_layout():
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, None) == _ws(64, 2, 384)
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, strides()) == _ws(64, 2, 384)
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, 64, 2, 384, BF16, None) == 0
+
+
+def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
+    S, B, H = 64, 2, 384
+    base, nb = _ws(S, B, H), S * B * H * 2
+    # [B,S,H] storage viewed as [S,B,H]: channels contiguous, strides even -> read in place
+    perm = [H, S * H, 1]
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, strides(gy=perm, x=perm)) == base
+    # channels strided -> gradY packed after the 256-aligned partials
+    st = strides(gy=[B * H * 2, H * 2, 2])
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, st) == -(-base // 256) * 256 + nb
+    # a base that is only 2-byte aligned cannot feed 4-byte lane loads -> x packed
+    assert mdc.mccb_get_workspace_size_ex(GY, X + 2, W, S, B, H, BF16, None) == \
+        -(-base // 256) * 256 + nb
+    # a transposed weight is packed (3*H elements)
+    got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, strides(w=[1, 3]))
+    assert got == -(-base // 256) * 256 + 3 * H * 2
+    # forward: in place needs row/batch strides that are multiples of 8 and a 16-byte base
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, BF16, strides(x=perm)) == 0
+    assert mdc.mccb_forward_get_workspace_size_ex(X + 8, W, S, B, H, BF16, None) == nb
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, BF16,
+                                                  strides(x=[B * H + 2, H, 1])) == nb
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
+def test_ex_null_required_pointer(which):
+    assert xcall(**{which: None}) == NULLPTR
+
+
+@pytest.mark.parametrize("field,idx", [("gradY", 0), ("gradY", 2), ("x", 1), ("weight", 0),
+                                       ("mask", 1)])
+def test_ex_negative_stride(field, idx):
+    st = strides()
+    getattr(st, field)[idx] = -1
+    assert xcall(st=st) == INVALID
+    if field != "mask":
+        with pytest.raises(mdc.MccbError):
+            mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, st)
+
+
+def test_ex_element_misaligned_input():
+    assert xcall(x=X + 1) == INVALID
+    assert xcall(gy=GY + 3) == INVALID
+    assert xcall(w=W + 1) == INVALID
+
+
+def test_ex_extent_overflow():
+    assert xcall(st=strides(gy=[1 << 60, 384, 1])) == INVALID
+
+
+def test_ex_outputs_must_not_overlap_strided_extents():
+    S, B, H = 64, 2, 384
+    # gradY stored [B,S,H]: its extent is the whole S*B*H block starting at GY
+    perm = [H, S * H, 1]
+    assert xcall(st=strides(gy=perm), gx=GY + S * H * 2) == INVALID
+    # a transposed mask [S,B] spans S*B bytes from M
+    assert xcall(st=strides(m=[1, B]), gw=M + 16) == INVALID
+    assert xcall(ws=X + 1024) == INVALID
+
+
+def test_ex_workspace_too_small():
+    need = mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, strides(gy=[768, 384, 2]))
+    assert xcall(st=strides(gy=[768, 384, 2]), wsz=need - 1) == INVALID
+
+
+def test_forward_ex_validation():
+    def f(**kw):
+        args = dict(x=X, w=W, m=M, y=GX, S=64, B=2, H=384, dt=BF16, st=None, ws=WS, wsz=1 << 40)
+        args.update(kw)
+        rc = mdc.mccb_forward_ex(args["x"], args["w"], args["m"], args["y"], args["S"], args["B"],
+                                 args["H"], args["dt"], args["st"], args["ws"], args["wsz"], None)
+        assert rc in VALIDATION_CODES, f"strided forward passed validation (rc={rc})"
+        return rc
+    assert f(x=None) == NULLPTR
+    assert f(st=strides(x=[768, -384, 1])) == INVALID
+    assert f(x=X + 1) == INVALID
+    assert f(y=X) == INVALID
+    assert f(y=GX + 8) == INVALID  # output stays 16-byte aligned
+    assert f(x=X + 2, ws=None) == NULLPTR  # packing needed, no workspace
+    assert f(S=0) == SHAPE
