@@ -10,7 +10,8 @@ bytes the method must move: read gradY and x, write gradX (2 bytes each per elem
 The same run also times the forward (mccb_forward, y = mask * causal conv(x, w)) on the same x,
 weight and mask, reported in the "forward" object of the same line: effective GB/s over its
 algorithmic bytes (read x, write y, read the mask and the weight); and both ops again on the same
-values stored [B,S,H] and passed as strided [S,B,H] views ("strided" object).
+values stored [B,S,H] and passed as strided [S,B,H] views ("strided" object), and with 2- and
+4-tap windows instead of the page's 3 ("taps" object).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -122,6 +123,8 @@ def main() -> int:
     ap.add_argument("--no-forward", action="store_true", help="skip timing the forward")
     ap.add_argument("--no-strided", action="store_true",
                     help="skip timing both ops on [B,S,H]-stored (strided) inputs")
+    ap.add_argument("--no-taps", action="store_true",
+                    help="skip timing both ops with 2- and 4-tap windows")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,7 +220,7 @@ def main() -> int:
         gy_p = gy.permute(1, 0, 2).contiguous().permute(1, 0, 2)
         x_p = x.permute(1, 0, 2).contiguous().permute(1, 0, 2)
         ws_p = torch.empty(max(1, mdc.mccb_get_workspace_size_ex(
-            gy_p.data_ptr(), x_p.data_ptr(), w.data_ptr(), wl.S, wl.B, wl.H,
+            gy_p.data_ptr(), x_p.data_ptr(), w.data_ptr(), wl.S, wl.B, wl.H, 3,
             mdc.DTYPE_CODE[gy.dtype], mdc._strides(gy_p, x_p, w, m))), dtype=torch.uint8,
             device=dev)
         y = torch.empty_like(x)
@@ -244,6 +247,42 @@ def main() -> int:
                                "ms_per_step": round(f_ms, 5)}}
         log(f"strided [B,S,H] inputs: backward {b_ms:.4f} ms, forward {f_ms:.4f} ms")
         del gy_p, x_p, ws_p, y
+        torch.cuda.empty_cache()
+
+    taps = None
+    if not args.no_taps:
+        taps = {}
+        for W in (2, 4):
+            wlw = wls.with_taps(wl, W)
+            ww = wls.weight_tensor(wlw, dev)
+            gww = torch.empty_like(ww)
+            ws_w = torch.empty(max(1, mdc.mccb_get_workspace_size_ex(
+                gy.data_ptr(), x.data_ptr(), ww.data_ptr(), wl.S, wl.B, wl.H, W,
+                mdc.DTYPE_CODE[gy.dtype], None)), dtype=torch.uint8, device=dev)
+            y = torch.empty_like(x)
+
+            def timed_w(fn):
+                for _ in range(args.warmup):
+                    fn()
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    fn()
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                return ev0.elapsed_time(ev1) / args.steps
+
+            b_ms = timed_w(lambda: mdc.backward(gy, x, ww, m, gradX=gx, gradWeight=gww,
+                                                workspace=ws_w, stream=stream))
+            f_ms = timed_w(lambda: mdc.forward(x, ww, m, y=y, stream=stream))
+            b_alg = wlw.algorithmic_bytes()
+            f_alg = 4 * wl.N + (wl.B * wl.S if m is not None else 0) + W * wl.H * 2
+            taps[f"W{W}"] = {"backward": {"value": round(b_alg / (b_ms * 1e-3) / 1e9, 1),
+                                          "unit": "GB/s", "ms_per_step": round(b_ms, 5)},
+                             "forward": {"value": round(f_alg / (f_ms * 1e-3) / 1e9, 1),
+                                         "unit": "GB/s", "ms_per_step": round(f_ms, 5)}}
+            log(f"W={W}: backward {b_ms:.4f} ms, forward {f_ms:.4f} ms")
+            del ww, gww, ws_w, y
         torch.cuda.empty_cache()
 
     ceiling = None
@@ -277,6 +316,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "forward": fwd,
         "strided": strided,
+        "taps": taps,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -133,36 +133,44 @@ typedef struct {
 } mccb_strides_t;
 
 /*
- * mccb_backward with strided inputs (strides NULL = all contiguous, same result as
- * mccb_backward). An input whose channels are contiguous (H stride 1) with even row and batch
- * strides and a 4-byte aligned base is read in place; any other gradY or x is first packed into a
- * contiguous copy inside the workspace (one extra read and write of that tensor), and a weight
- * that is not contiguous and 16-byte aligned is packed too. The mask is read through its strides.
- * Phase 1 therefore takes the input pointers as well (as the page's phase 1 takes the tensors):
- * they are inspected for alignment only, never dereferenced. Input bases need 2-byte alignment;
- * gradX, gradWeight and the workspace stay contiguous and 16-byte aligned. Negative strides, or an
- * input extent past 2^62 bytes, give MCCB_ERR_PARAM_INVALID; no output or the workspace may
- * overlap any input's extent. Otherwise as mccb_get_workspace_size / mccb_backward.
+ * Extended calls: strided inputs and a window of W taps.
+ *
+ * W: the weight and gradWeight are [W,H]; the equations of the function description with 2 (and
+ * the forward's look-back) replaced by W-1. The constraints section supports only W = 3 "for
+ * now"; the kernels here take W = 1..4 (other values: MCCB_ERR_SHAPE). W = 3 with NULL strides is
+ * exactly mccb_get_workspace_size / mccb_backward / mccb_forward.
+ *
+ * Strides (NULL = all contiguous): an input whose channels are contiguous (H stride 1) with even
+ * row and batch strides and a 4-byte aligned base is read in place by the backward; any other
+ * gradY or x is first packed into a contiguous copy inside the workspace (one extra read and write
+ * of that tensor), and a weight that is not contiguous and 16-byte aligned is packed too. The mask
+ * is read through its strides. Phase 1 therefore takes the input pointers as well (as the page's
+ * phase 1 takes the tensors): they are inspected for alignment only, never dereferenced. Input
+ * bases need 2-byte alignment; gradX, gradWeight and the workspace stay contiguous and 16-byte
+ * aligned. Negative strides, or an input extent past 2^62 bytes, give MCCB_ERR_PARAM_INVALID; no
+ * output or the workspace may overlap any input's extent. Otherwise as mccb_get_workspace_size /
+ * mccb_backward.
  */
 int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *weight, int64_t S,
-                               int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
-                               uint64_t *workspace_size);
+                               int64_t B, int64_t H, int64_t W, int dtype,
+                               const mccb_strides_t *strides, uint64_t *workspace_size);
 int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
-                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
-                     const mccb_strides_t *strides, void *workspace, uint64_t workspace_size,
-                     void *stream);
+                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int64_t W,
+                     int dtype, const mccb_strides_t *strides, void *workspace,
+                     uint64_t workspace_size, void *stream);
 
 /*
- * mccb_forward with strided x, weight and mask (strides->gradY is ignored). x is read in place
- * when its channels are contiguous, its row and batch strides are multiples of 8 and its base is
- * 16-byte aligned; otherwise it (and a non-contiguous weight) is packed into the workspace,
- * whose size phase 1 returns (0 when nothing needs packing; the workspace may then be NULL).
+ * mccb_forward with strided x, weight and mask (strides->gradY is ignored) and W taps:
+ * y[i] = mask[j,i] * sum_{k=0}^{W-1} weight[k] * x[i-W+1+k]. x is read in place when its channels
+ * are contiguous, its row and batch strides are multiples of 8 and its base is 16-byte aligned;
+ * otherwise it (and a non-contiguous weight) is packed into the workspace, whose size phase 1
+ * returns (0 when nothing needs packing; the workspace may then be NULL).
  */
 int mccb_forward_get_workspace_size_ex(const void *x, const void *weight, int64_t S, int64_t B,
-                                       int64_t H, int dtype, const mccb_strides_t *strides,
-                                       uint64_t *workspace_size);
+                                       int64_t H, int64_t W, int dtype,
+                                       const mccb_strides_t *strides, uint64_t *workspace_size);
 int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
-                    int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                    int64_t B, int64_t H, int64_t W, int dtype, const mccb_strides_t *strides,
                     void *workspace, uint64_t workspace_size, void *stream);
 
 /* The tiling chosen for a shape, for mccb_backward (first eight fields) and mccb_forward (fwd_*);

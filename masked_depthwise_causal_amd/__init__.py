@@ -58,10 +58,10 @@ def mccb_forward(x: int, weight: int, mask: int | None, y: int, S: int, B: int, 
     return int(lib().mccb_forward(x, weight, mask, y, S, B, H, dtype, stream))
 
 
-def mccb_get_workspace_size_ex(gradY: int, x: int, weight: int, S: int, B: int, H: int, dtype: int,
-                               strides: Strides | None) -> int:
+def mccb_get_workspace_size_ex(gradY: int, x: int, weight: int, S: int, B: int, H: int, W: int,
+                               dtype: int, strides: Strides | None) -> int:
     out = ctypes.c_uint64(0)
-    rc = lib().mccb_get_workspace_size_ex(gradY, x, weight, S, B, H, dtype,
+    rc = lib().mccb_get_workspace_size_ex(gradY, x, weight, S, B, H, W, dtype,
                                           None if strides is None else ctypes.byref(strides),
                                           ctypes.byref(out))
     if rc != MCCB_OK:
@@ -70,31 +70,31 @@ def mccb_get_workspace_size_ex(gradY: int, x: int, weight: int, S: int, B: int, 
 
 
 def mccb_backward_ex(gradY: int, x: int, weight: int, mask: int | None, gradX: int,
-                     gradWeight: int, S: int, B: int, H: int, dtype: int,
+                     gradWeight: int, S: int, B: int, H: int, W: int, dtype: int,
                      strides: Strides | None, workspace: int | None, workspace_size: int,
                      stream: int | None) -> int:
     """Raw call with integer device addresses; returns the status code (does not raise)."""
-    return int(lib().mccb_backward_ex(gradY, x, weight, mask, gradX, gradWeight, S, B, H, dtype,
+    return int(lib().mccb_backward_ex(gradY, x, weight, mask, gradX, gradWeight, S, B, H, W, dtype,
                                       None if strides is None else ctypes.byref(strides),
                                       workspace, workspace_size, stream))
 
 
-def mccb_forward_get_workspace_size_ex(x: int, weight: int, S: int, B: int, H: int, dtype: int,
-                                       strides: Strides | None) -> int:
+def mccb_forward_get_workspace_size_ex(x: int, weight: int, S: int, B: int, H: int, W: int,
+                                       dtype: int, strides: Strides | None) -> int:
     out = ctypes.c_uint64(0)
     rc = lib().mccb_forward_get_workspace_size_ex(
-        x, weight, S, B, H, dtype, None if strides is None else ctypes.byref(strides),
+        x, weight, S, B, H, W, dtype, None if strides is None else ctypes.byref(strides),
         ctypes.byref(out))
     if rc != MCCB_OK:
         raise MccbError(rc, "mccb_forward_get_workspace_size_ex")
     return int(out.value)
 
 
-def mccb_forward_ex(x: int, weight: int, mask: int | None, y: int, S: int, B: int, H: int,
+def mccb_forward_ex(x: int, weight: int, mask: int | None, y: int, S: int, B: int, H: int, W: int,
                     dtype: int, strides: Strides | None, workspace: int | None,
                     workspace_size: int, stream: int | None) -> int:
     """Raw call with integer device addresses; returns the status code (does not raise)."""
-    return int(lib().mccb_forward_ex(x, weight, mask, y, S, B, H, dtype,
+    return int(lib().mccb_forward_ex(x, weight, mask, y, S, B, H, W, dtype,
                                      None if strides is None else ctypes.byref(strides),
                                      workspace, workspace_size, stream))
 
@@ -160,7 +160,8 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
              mask: torch.Tensor | None = None, gradX: torch.Tensor | None = None,
              gradWeight: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
              stream: torch.cuda.Stream | None = None):
-    """gradX [S,B,H], gradWeight [3,H] on device tensors (outputs allocated if None).
+    """gradX [S,B,H], gradWeight [W,H] on device tensors (outputs allocated if None); the window W
+    is the weight's first dimension (3 on the page; 1..4 accepted).
 
     The inputs may be strided views (mccb_backward_ex); the outputs must be contiguous. Enqueues
     on `stream` (default: torch's current stream) and returns without synchronizing.
@@ -174,7 +175,10 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
         raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
     _check_tensor("gradY", gradY, (S, B, H), dt, dev, contiguous=False)
     _check_tensor("x", x, (S, B, H), dt, dev, contiguous=False)
-    _check_tensor("weight", weight, (3, H), dt, dev, contiguous=False)
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a [W,H] tensor")
+    W = int(weight.shape[0])
+    _check_tensor("weight", weight, (W, H), dt, dev, contiguous=False)
     if mask is not None:
         _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
@@ -182,13 +186,13 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     if gradX is None:
         gradX = torch.empty((S, B, H), dtype=dt, device=dev)
     if gradWeight is None:
-        gradWeight = torch.empty((3, H), dtype=dt, device=dev)
+        gradWeight = torch.empty((W, H), dtype=dt, device=dev)
     _check_tensor("gradX", gradX, (S, B, H), dt, dev)
-    _check_tensor("gradWeight", gradWeight, (3, H), dt, dev)
+    _check_tensor("gradWeight", gradWeight, (W, H), dt, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     strides = _strides(gradY, x, weight, mask)
     mptr = None if mask is None else mask.data_ptr()
-    if strides is None:
+    if strides is None and W == 3:
         if workspace is None:
             workspace = workspace_for(S, B, H, dt, dev)
         rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
@@ -198,10 +202,10 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     else:
         if workspace is None:
             n = mccb_get_workspace_size_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), S, B,
-                                           H, DTYPE_CODE[dt], strides)
+                                           H, W, DTYPE_CODE[dt], strides)
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         rc = mccb_backward_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
-                              gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt],
+                              gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, W, DTYPE_CODE[dt],
                               strides, workspace.data_ptr(), workspace.numel(), st.cuda_stream)
         where = "mccb_backward_ex"
     if rc != MCCB_OK:
@@ -213,8 +217,9 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
             y: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y [S,B,H] = mask * causal depthwise conv(x, weight) on device tensors (y allocated if
-    None). The inputs may be strided views (mccb_forward_ex); y must be contiguous. Enqueues on
-    `stream` (default: torch's current stream) without synchronizing."""
+    None); the window W is the weight's first dimension (3 on the page; 1..4 accepted). The inputs
+    may be strided views (mccb_forward_ex); y must be contiguous. Enqueues on `stream` (default:
+    torch's current stream) without synchronizing."""
     if x.dim() != 3:
         raise ValueError("x must be [S,B,H]")
     S, B, H = (int(s) for s in x.shape)
@@ -222,7 +227,10 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
     if dt not in DTYPE_CODE:
         raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
     _check_tensor("x", x, (S, B, H), dt, dev, contiguous=False)
-    _check_tensor("weight", weight, (3, H), dt, dev, contiguous=False)
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a [W,H] tensor")
+    W = int(weight.shape[0])
+    _check_tensor("weight", weight, (W, H), dt, dev, contiguous=False)
     if mask is not None:
         _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
@@ -233,16 +241,16 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     strides = _strides(None, x, weight, mask)
     mptr = None if mask is None else mask.data_ptr()
-    if strides is None:
+    if strides is None and W == 3:
         rc = mccb_forward(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H,
                           DTYPE_CODE[dt], st.cuda_stream)
         where = "mccb_forward"
     else:
         if workspace is None:
-            n = mccb_forward_get_workspace_size_ex(x.data_ptr(), weight.data_ptr(), S, B, H,
+            n = mccb_forward_get_workspace_size_ex(x.data_ptr(), weight.data_ptr(), S, B, H, W,
                                                    DTYPE_CODE[dt], strides)
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-        rc = mccb_forward_ex(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H,
+        rc = mccb_forward_ex(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H, W,
                              DTYPE_CODE[dt], strides, workspace.data_ptr(), workspace.numel(),
                              st.cuda_stream)
         where = "mccb_forward_ex"

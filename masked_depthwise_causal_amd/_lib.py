@@ -49,16 +49,17 @@ def lib() -> ctypes.CDLL:
         L.mccb_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
         L.mccb_forward.restype = ctypes.c_int
         sp = ctypes.POINTER(Strides)
-        L.mccb_get_workspace_size_ex.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, sp,
+        L.mccb_get_workspace_size_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, sp,
                                                  ctypes.POINTER(u64)]
         L.mccb_get_workspace_size_ex.restype = ctypes.c_int
-        L.mccb_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, sp,
-                                       vp, u64, vp]
+        L.mccb_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                       sp, vp, u64, vp]
         L.mccb_backward_ex.restype = ctypes.c_int
-        L.mccb_forward_get_workspace_size_ex.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, sp,
-                                                         ctypes.POINTER(u64)]
+        L.mccb_forward_get_workspace_size_ex.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                                         sp, ctypes.POINTER(u64)]
         L.mccb_forward_get_workspace_size_ex.restype = ctypes.c_int
-        L.mccb_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, sp, vp, u64, vp]
+        L.mccb_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, sp, vp, u64,
+                                      vp]
         L.mccb_forward_ex.restype = ctypes.c_int
         L.mccb_status_string.argtypes = [ctypes.c_int]
         L.mccb_status_string.restype = ctypes.c_char_p

@@ -123,6 +123,7 @@ typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
 
 constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
+constexpr int64_t kMinW = 1, kMaxW = 4;  // window taps supported by the kernels
 constexpr int64_t kStripRows = MCCB_STRIP_ROWS;
 constexpr int64_t kMinBlocks = MCCB_MIN_BLOCKS;
 constexpr int64_t kMinStripRows = MCCB_MIN_STRIP_ROWS;
@@ -192,33 +193,30 @@ __device__ static inline void store_vec(vec_t *p, vec_t v) {
 #endif
 }
 
-// gradX for one lane's kVec columns at row i from the masked gradY rows i, i+1, i+2 (fp64), and
-// the gradWeight terms of row i: a_k += gYm[i+2-k] * x[i]. Returns the packed gradX row.
-template <int DT>
-__device__ static inline vec_t stencil_row(const double (&d0)[kVec], const double (&d1)[kVec],
-                                           const double (&d2)[kVec], const vec_t x_row,
-                                           const double (&w0)[kVec], const double (&w1)[kVec],
-                                           const double (&w2)[kVec], double (&a0)[kVec],
-                                           double (&a1)[kVec], double (&a2)[kVec]) {
+// gradX for one lane's kVec columns at row i from the masked gradY rows i .. i+W-1 (fp64, d[k] =
+// gYm[i+k]), and the gradWeight terms of row i: a[k] += gYm[i+W-1-k] * x[i]. Returns the packed
+// gradX row.
+template <int DT, int W>
+__device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec_t x_row,
+                                           const double (&wt)[W][kVec], double (&a)[W][kVec]) {
     float xf[kVec];
     unpack_vec<DT>(x_row, xf);
     float out[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        // gradX[i] = gYm[i]*w[2] + gYm[i+1]*w[1] + gYm[i+2]*w[0] (products exact in fp64)
-        double s = d0[e] * w2[e];
-        s = __builtin_fma(d1[e], w1[e], s);
-        s = __builtin_fma(d2[e], w0[e], s);
+        // gradX[i] = sum_k gYm[i+k] * w[W-1-k], in k order (each product exact in fp64)
+        double s = d[0][e] * wt[W - 1][e];
+#pragma unroll
+        for (int k = 1; k < W; ++k) s = __builtin_fma(d[k][e], wt[W - 1 - k][e], s);
 #if MCCB_EXACT_GRADX
         out[e] = round_to_odd_f32(s);
 #else
         out[e] = (float)s;
 #endif
-        // gradWeight[k] += gYm[i+2-k] * x[i]
+        // gradWeight[k] += gYm[i+W-1-k] * x[i]
         const double xd = (double)xf[e];
-        a2[e] = __builtin_fma(d0[e], xd, a2[e]);
-        a1[e] = __builtin_fma(d1[e], xd, a1[e]);
-        a0[e] = __builtin_fma(d2[e], xd, a0[e]);
+#pragma unroll
+        for (int k = 0; k < W; ++k) a[k][e] = __builtin_fma(d[W - 1 - k][e], xd, a[k][e]);
     }
     vec_t r;
 #pragma unroll
@@ -235,10 +233,11 @@ __device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Kernel 1: mask + gradX + gradWeight partials in one HBM pass.
+// Kernel 1: mask + gradX + gradWeight partials in one HBM pass, for a window of W taps (the
+// look-ahead is W-1 rows).
 // grid.x = n_col_blocks * n_strips (column block fastest), block = kColGroups * kRing waves.
-// Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + 2) mask bytes.
-// Workspace: fp64 partials [n_strips][3][C].
+// Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + W - 1) mask bytes.
+// Workspace: fp64 partials [n_strips][W][C].
 // ---------------------------------------------------------------------------------------------
 // Input strides (in elements; channels contiguous, so only the row and batch strides vary): a
 // contiguous [S,B,H] tensor has row stride B*H and batch stride H. With STRIDED false the kernel
@@ -251,15 +250,21 @@ struct InStrides {
     int64_t gy_row, gy_batch, x_row, x_batch, m_batch, m_row;
 };
 
-// The strided variant keeps a second lane offset and row stride; it is compiled for one wavefront
-// less per SIMD so that it does not spill.
-template <int DT, bool HAS_MASK, bool STRIDED>
+// Register budget: the strided variant keeps a second lane offset and row stride, and a wider
+// window keeps more fp64 state; such variants are compiled for one wavefront less per SIMD so that
+// they do not spill.
+constexpr int fused_waves_per_simd(bool strided, int w) {
+    return (strided || w > 3) ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD;
+}
+
+template <int DT, bool HAS_MASK, bool STRIDED, int W>
 __global__ void __launch_bounds__(kBlockWaves *kWave)
-    __attribute__((amdgpu_waves_per_eu(STRIDED ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD)))
+    __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(STRIDED, W))))
     mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
                    const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
                    vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
                    int64_t rows_per_strip, int64_t n_col_blocks, InStrides st) {
+    constexpr int L = W - 1;  // look-ahead rows
     extern __shared__ uint8_t smask[];
     __shared__ f64x2 red[kBlockWaves][kWave * kVec / 2];
 
@@ -290,7 +295,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
         const int64_t c_last = (c_first + kBlockCols < C ? c_first + kBlockCols : C) - 1;
         const int64_t j_first = c_first / H;
         const int nj = (int)(c_last / H - j_first + 1);
-        const int span = (int)(rows_per_strip + 2);
+        const int span = (int)(rows_per_strip + L);
         for (int t = threadIdx.x; t < nj * span; t += blockDim.x) {
             const int jj = t / span;
             const int64_t row = rs0 + (t - jj * span);
@@ -300,23 +305,20 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
         __syncthreads();
     }
 
-    double w0[kVec], w1[kVec], w2[kVec];
-    {
+    double wt[W][kVec];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
         float t[kVec];
-        unpack_vec<DT>(w[(0 * H + h) / kVec], t);
+        unpack_vec<DT>(w[(k * H + h) / kVec], t);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) w0[e] = (double)t[e];
-        unpack_vec<DT>(w[(1 * H + h) / kVec], t);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) w1[e] = (double)t[e];
-        unpack_vec<DT>(w[(2 * H + h) / kVec], t);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) w2[e] = (double)t[e];
+        for (int e = 0; e < kVec; ++e) wt[k][e] = (double)t[e];
     }
 
-    double a0[kVec], a1[kVec], a2[kVec];
+    double a[W][kVec];
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) a0[e] = a1[e] = a2[e] = 0.0;
+    for (int k = 0; k < W; ++k)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) a[k][e] = 0.0;
 
     vec_t zero;
 #pragma unroll
@@ -352,37 +354,36 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     // A turn is "whole" when this wave's kTurnRows rows and their look-ahead rows all exist.
     auto whole = [&](int64_t r0) {
         const int64_t i0 = r0 + ring * kTurnRows;
-        return i0 + kTurnRows <= rs1 && i0 + kTurnRows + 2 <= S;
+        return i0 + kTurnRows <= rs1 && i0 + kTurnRows + L <= S;
     };
-    // Issue the loads of a whole turn: gradY rows i0 .. i0+kTurnRows+1 and x rows i0 ..
-    // i0+kTurnRows-1. Rows i0, i0+1 were the previous wave's last look-ahead rows, and this wave's
-    // last two are the next wave's first: cached loads, so those come from L2; the rest stream.
-    auto issue = [&](int64_t r0, vec_t (&qy)[kTurnRows + 2], vec_t (&qx)[kTurnRows]) {
+    // Issue the loads of a whole turn: gradY rows i0 .. i0+kTurnRows+L-1 and x rows i0 ..
+    // i0+kTurnRows-1. The first L gradY rows were the previous wave's last look-ahead rows, and this
+    // wave's last L are the next wave's first: cached loads, so those come from L2; the rest stream.
+    auto issue = [&](int64_t r0, vec_t (&qy)[kTurnRows + L], vec_t (&qx)[kTurnRows]) {
         const int64_t i0 = r0 + ring * kTurnRows;
-        qy[0] = load_vec_cached(at_gy(i0));
-        qy[1] = load_vec_cached(at_gy(i0 + 1));
+#pragma unroll
+        for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(at_gy(i0 + k));
 #pragma unroll
         for (int u = 0; u < kTurnRows; ++u) {
-            qy[u + 2] = (u + 2 >= kTurnRows) ? load_vec_cached(at_gy(i0 + 2 + u))
-                                             : load_vec(at_gy(i0 + 2 + u));
+            qy[u + L] = (u + L >= kTurnRows) ? load_vec_cached(at_gy(i0 + L + u))
+                                             : load_vec(at_gy(i0 + L + u));
             qx[u] = load_vec(at_x(i0 + u));
         }
     };
-    auto compute = [&](int64_t r0, const vec_t (&qy)[kTurnRows + 2], const vec_t (&qx)[kTurnRows]) {
+    auto compute = [&](int64_t r0, const vec_t (&qy)[kTurnRows + L], const vec_t (&qx)[kTurnRows]) {
         const int64_t i0 = r0 + ring * kTurnRows;
-        double d0[kVec], d1[kVec], d2[kVec];
-        widen<DT>(keep(i0) ? qy[0] : zero, d0);
-        widen<DT>(keep(i0 + 1) ? qy[1] : zero, d1);
+        double d[W][kVec];
+#pragma unroll
+        for (int k = 0; k < L; ++k) widen<DT>(keep(i0 + k) ? qy[k] : zero, d[k]);
 #pragma unroll
         for (int u = 0; u < kTurnRows; ++u) {
-            widen<DT>(keep(i0 + 2 + u) ? qy[u + 2] : zero, d2);
-            const vec_t r = stencil_row<DT>(d0, d1, d2, qx[u], w0, w1, w2, a0, a1, a2);
+            widen<DT>(keep(i0 + L + u) ? qy[u + L] : zero, d[L]);
+            const vec_t r = stencil_row<DT, W>(d, qx[u], wt, a);
             if (active) store_vec(out_at(i0 + u), r);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                d0[e] = d1[e];
-                d1[e] = d2[e];
-            }
+            for (int k = 0; k < L; ++k)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) d[k][e] = d[k + 1][e];
         }
     };
     // Partial turn at the end of the strip or of the tensor: one row at a time, gradY rows past S
@@ -391,24 +392,24 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
         const int64_t i0 = r0 + ring * kTurnRows;
         if (i0 >= rs1) return;
         const int64_t i1 = (i0 + kTurnRows < rs1) ? i0 + kTurnRows : rs1;
-        double d0[kVec], d1[kVec], d2[kVec];
-        widen<DT>((i0 < S && keep(i0)) ? load_vec_cached(at_gy(i0)) : zero, d0);
-        widen<DT>((i0 + 1 < S && keep(i0 + 1)) ? load_vec_cached(at_gy(i0 + 1)) : zero, d1);
+        double d[W][kVec];
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            widen<DT>((i0 + k < S && keep(i0 + k)) ? load_vec_cached(at_gy(i0 + k)) : zero, d[k]);
         for (int64_t i = i0; i < i1; ++i) {
-            widen<DT>((i + 2 < S && keep(i + 2)) ? load_vec_cached(at_gy(i + 2)) : zero, d2);
-            const vec_t r = stencil_row<DT>(d0, d1, d2, load_vec(at_x(i)), w0, w1, w2, a0, a1, a2);
+            widen<DT>((i + L < S && keep(i + L)) ? load_vec_cached(at_gy(i + L)) : zero, d[L]);
+            const vec_t r = stencil_row<DT, W>(d, load_vec(at_x(i)), wt, a);
             if (active) store_vec(out_at(i), r);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                d0[e] = d1[e];
-                d1[e] = d2[e];
-            }
+            for (int k = 0; k < L; ++k)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) d[k][e] = d[k + 1][e];
         }
     };
     // One round: prefetch the next round's whole turn into `nxt`, then compute this round from
     // `cur` (loaded one round earlier) while those loads are in flight.
-    auto round = [&](int64_t r0, const vec_t (&cy)[kTurnRows + 2], const vec_t (&cx)[kTurnRows],
-                     vec_t (&ny)[kTurnRows + 2], vec_t (&nx)[kTurnRows]) {
+    auto round = [&](int64_t r0, const vec_t (&cy)[kTurnRows + L], const vec_t (&cx)[kTurnRows],
+                     vec_t (&ny)[kTurnRows + L], vec_t (&nx)[kTurnRows]) {
         const int64_t rn = r0 + kRoundRows;
         if (rn < rs1 && whole(rn)) issue(rn, ny, nx);
         if (whole(r0))
@@ -422,7 +423,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 #endif
     };
 
-    vec_t ay[kTurnRows + 2], ax[kTurnRows], by[kTurnRows + 2], bx[kTurnRows];
+    vec_t ay[kTurnRows + L], ax[kTurnRows], by[kTurnRows + L], bx[kTurnRows];
     if (whole(rs0)) issue(rs0, ay, ax);
     // Unrolled by two so that the two register buffers swap roles without copies.
     for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * kRoundRows) {
@@ -434,12 +435,12 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     // gradWeight partials of the strip: for each column group add its kRing waves in a fixed
     // order (ring position 0 first).
     const int64_t col0 = col_block * kBlockCols;
-    for (int k = 0; k < 3; ++k) {
-        const double *acc = (k == 0) ? a0 : (k == 1) ? a1 : a2;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
         __syncthreads();
 #pragma unroll
         for (int p = 0; p < kVec / 2; ++p)
-            red[wave][lane * (kVec / 2) + p] = f64x2{acc[2 * p], acc[2 * p + 1]};
+            red[wave][lane * (kVec / 2) + p] = f64x2{a[k][2 * p], a[k][2 * p + 1]};
         __syncthreads();
         const double *flat = reinterpret_cast<const double *>(&red[0][0]);
         for (int t = threadIdx.x; t < kBlockCols; t += blockDim.x) {
@@ -448,7 +449,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 #pragma unroll
             for (int q = 1; q < kRing; ++q) s += flat[(q * kColGroups + g) * kGroupCols + within];
             const int64_t col = col0 + t;
-            if (col < C) ws[(strip * 3 + k) * C + col] = s;
+            if (col < C) ws[(strip * W + k) * C + col] = s;
         }
     }
 }
@@ -456,7 +457,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 // ---------------------------------------------------------------------------------------------
 // Kernel 2: gradWeight[k,h] = sum over strips s (outer) and batches j (inner) of
 // ws[s][k][j*H + h], in fp64, then one rounding to the dtype.
-// grid = (ceil(H / 128), 3), block = kReduceWaves * 64 lanes; a lane owns 2 channels. Each wave
+// grid = (ceil(H / 128), W), block = kReduceWaves * 64 lanes; a lane owns 2 channels. Each wave
 // sums a contiguous range of the (s, j) rows; the waves' sums are then added in wave order.
 // ---------------------------------------------------------------------------------------------
 template <int DT>
@@ -467,6 +468,7 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int k = blockIdx.y;
+    const int W = gridDim.y;  // taps
     const int64_t h = (int64_t)blockIdx.x * kReduceCols + lane * 2;
     const int64_t C = B * H;
     const int64_t rows = n_strips * B;
@@ -479,7 +481,7 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
         int64_t s = lo / B, jj = lo - (lo / B) * B;
 #pragma unroll 4
         for (int64_t r = lo; r < hi; ++r) {
-            acc += *reinterpret_cast<const f64x2 *>(ws + (s * 3 + k) * C + jj * H + h);
+            acc += *reinterpret_cast<const f64x2 *>(ws + (s * W + k) * C + jj * H + h);
             if (++jj == B) {
                 jj = 0;
                 ++s;
@@ -498,20 +500,20 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
 
 
 // ---------------------------------------------------------------------------------------------
-// Forward kernel: y[i,c] = mask[j,i] * (w[0,h] x[i-2,c] + w[1,h] x[i-1,c] + w[2,h] x[i,c]), with
-// c = j*H + h and rows i-2, i-1 < 0 read as 0 (the causal depthwise conv the backward above
-// differentiates). Pure streaming: read x, write y, nothing to reduce.
+// Forward kernel: y[i,c] = mask[j,i] * sum_{k=0}^{W-1} w[k,h] x[i-W+1+k, c], with c = j*H + h and
+// rows before 0 read as 0 (the causal depthwise conv the backward above differentiates; W = 3 on
+// the page). Pure streaming: read x, write y, nothing to reduce.
 //
 // A block covers a short tile: kFwdRows rows x kFwdCols contiguous columns (kFwdWaves wavefronts
-// side by side, kFwdVec channels per lane; 8 rows x 4096 columns by default). Tiles are numbered row-major, column tile fastest, so
-// the blocks in flight at any moment sit on a few neighbouring rows; the HBM serves such a compact
-// front markedly faster than many independent column walks. The two rows before the tile are
-// re-read with cached loads (the tile above loaded them, also cached, as its last two rows); when
-// the column-tile count is a multiple of the 8 XCDs, which take blocks round-robin, a tile and the
-// tile above it run on the same XCD and the re-read hits its L2.
+// side by side, kFwdVec channels per lane; 8 rows x 4096 columns by default). Tiles are numbered
+// row-major, column tile fastest, so the blocks in flight at any moment sit on a few neighbouring
+// rows; the HBM serves such a compact front markedly faster than many independent column walks.
+// The W-1 rows before the tile are re-read with cached loads (the tile above loaded them, also
+// cached, as its last rows); when the column-tile count is a multiple of the 8 XCDs, which take
+// blocks round-robin, a tile and the tile above it run on the same XCD and the re-read hits its L2.
 //
-// Every output is the exact three-term sum (products of 16-bit values are exact in fp64) rounded
-// once: round-to-odd to fp32, then round-to-nearest-even to the dtype.
+// Every output is the exact W-term sum (products of 16-bit values are exact in fp64) rounded once:
+// round-to-odd to fp32, then round-to-nearest-even to the dtype.
 // ---------------------------------------------------------------------------------------------
 constexpr int kFwdVec = MCCB_FWD_VEC;
 constexpr int kFwdWords = kFwdVec / 2;
@@ -519,7 +521,7 @@ constexpr int kFwdWaves = MCCB_FWD_WAVES;
 constexpr int kFwdRows = MCCB_FWD_ROWS;
 constexpr int kFwdCols = kFwdWaves * kWave * kFwdVec;  // columns of one tile
 static_assert(kFwdVec == 2 || kFwdVec == 4 || kFwdVec == 8, "forward lane vector: 4, 8 or 16 bytes");
-static_assert(kFwdRows >= 2, "the two look-back rows come from the tile above");
+static_assert(kFwdRows >= 3, "the look-back rows (up to 3) come from the tile above");
 static_assert(kFwdWaves * kWave <= 1024, "forward block too large");
 
 typedef uint32_t fvec_t __attribute__((ext_vector_type(kFwdWords)));
@@ -535,11 +537,12 @@ __device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
     }
 }
 
-template <int DT, bool HAS_MASK, bool STRIDED>
+template <int DT, bool HAS_MASK, bool STRIDED, int W>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
              int64_t H, int64_t n_ct, InStrides st) {
+    constexpr int L = W - 1;  // look-back rows
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
     if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
     const int64_t ct = blockIdx.x % n_ct;  // column tile (fastest)
@@ -555,25 +558,24 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     const int64_t j = c0 / H;
     const int64_t r0 = rt * kFwdRows;
 
-    // x rows r0-2 .. r0+kFwdRows-1; rows outside [0, S) are zero
-    fvec_t xr[kFwdRows + 2];
+    // x rows r0-L .. r0+kFwdRows-1; rows outside [0, S) are zero
+    fvec_t xr[kFwdRows + L];
 #pragma unroll
-    for (int u = 0; u < kFwdRows + 2; ++u) {
-        const int64_t row = r0 - 2 + u;
+    for (int u = 0; u < kFwdRows + L; ++u) {
+        const int64_t row = r0 - L + u;
         fvec_t q = {};
         if (row >= 0 && row < S) {
             const fvec_t *p = STRIDED ? reinterpret_cast<const fvec_t *>(
                                             reinterpret_cast<const char *>(x) +
                                             (row * st.x_row + j * st.x_batch + h0) * 2)
                                       : x + row * CV + v;
-            q = (u < 2 || u >= kFwdRows) ? *p : __builtin_nontemporal_load(p);
+            q = (u < L || u >= kFwdRows) ? *p : __builtin_nontemporal_load(p);
         }
         xr[u] = q;
     }
-    double w0[kFwdVec], w1[kFwdVec], w2[kFwdVec];
-    widen_f<DT>(w[(0 * H + h0) / kFwdVec], w0);
-    widen_f<DT>(w[(1 * H + h0) / kFwdVec], w1);
-    widen_f<DT>(w[(2 * H + h0) / kFwdVec], w2);
+    double wt[W][kFwdVec];
+#pragma unroll
+    for (int k = 0; k < W; ++k) widen_f<DT>(w[(k * H + h0) / kFwdVec], wt[k]);
     uint8_t keep[kFwdRows];
 #pragma unroll
     for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
@@ -583,20 +585,20 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
         for (int u = 0; u < kFwdRows; ++u) keep[u] = (r0 + u < S) ? mrow[u * st.m_row] : 0;
     }
 
-    double a[kFwdVec], b[kFwdVec], c[kFwdVec];
-    widen_f<DT>(xr[0], a);
-    widen_f<DT>(xr[1], b);
+    double win[W][kFwdVec];  // win[k] = x row i-L+k
+#pragma unroll
+    for (int k = 0; k < L; ++k) widen_f<DT>(xr[k], win[k]);
 #pragma unroll
     for (int u = 0; u < kFwdRows; ++u) {
         const int64_t row = r0 + u;
-        widen_f<DT>(xr[u + 2], c);
+        widen_f<DT>(xr[u + L], win[L]);
         float out[kFwdVec];
 #pragma unroll
         for (int e = 0; e < kFwdVec; ++e) {
-            // y[i] = w[0] x[i-2] + w[1] x[i-1] + w[2] x[i], exact in fp64, rounded once
-            double s = a[e] * w0[e];
-            s = __builtin_fma(b[e], w1[e], s);
-            s = __builtin_fma(c[e], w2[e], s);
+            // y[i] = sum_k w[k] x[i-L+k], in k order, exact in fp64, rounded once
+            double s = win[0][e] * wt[0][e];
+#pragma unroll
+            for (int k = 1; k < W; ++k) s = __builtin_fma(win[k][e], wt[k][e], s);
             out[e] = keep[u] ? round_to_odd_f32(s) : 0.0f;
         }
         fvec_t r;
@@ -604,10 +606,9 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
         for (int p = 0; p < kFwdWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
         if (row < S) __builtin_nontemporal_store(r, y + row * CV + v);
 #pragma unroll
-        for (int e = 0; e < kFwdVec; ++e) {
-            a[e] = b[e];
-            b[e] = c[e];
-        }
+        for (int k = 0; k < L; ++k)
+#pragma unroll
+            for (int e = 0; e < kFwdVec; ++e) win[k][e] = win[k + 1][e];
     }
 }
 
@@ -635,7 +636,7 @@ __global__ void __launch_bounds__(256)
 // ---------------------------------------------------------------------------------------------
 struct Plan {
     int64_t S, B, H, C;
-    int dtype;
+    int dtype, W;
     int64_t rows_per_strip, n_strips, n_col_blocks;
     uint64_t ws_bytes;
     size_t mask_lds;
@@ -648,21 +649,25 @@ int check_shape(int64_t S, int64_t B, int64_t H, int dtype) {
     return MCCB_OK;
 }
 
-// Pure function of (S, B, H, dtype) -- never of the device -- so gradWeight's summation order, and
-// therefore its bits, are the same on every run and every MI355X.
-Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype) {
+// Window taps W (the weight's first dimension): 3 on the page; 1..4 here.
+int check_taps(int64_t W) { return (W >= kMinW && W <= kMaxW) ? MCCB_OK : MCCB_ERR_SHAPE; }
+
+// Pure function of (S, B, H, dtype, W) -- never of the device -- so gradWeight's summation order,
+// and therefore its bits, are the same on every run and every MI355X.
+Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype, int W = 3) {
     Plan p;
     p.S = S;
     p.B = B;
     p.H = H;
     p.C = B * H;
     p.dtype = dtype;
+    p.W = W;
     p.n_col_blocks = (p.C + kBlockCols - 1) / kBlockCols;
     // Split the rows into strips of about kStripRows rows, more if the grid would have fewer than
     // kMinBlocks blocks (too few to keep every CU busy), but none shorter than kMinStripRows rows;
     // strips are a whole number of rounds long. Short-lived blocks keep the rows in flight across
     // the GPU close together, which the HBM serves faster than long independent column walks; each
-    // strip costs 24 bytes per column of partials written and read back, against 6 bytes per
+    // strip costs 8*W bytes per column of partials written and read back, against 6 bytes per
     // element streamed.
     const int64_t max_strips = (S + kRoundRows - 1) / kRoundRows;
     int64_t strips = (S + kStripRows - 1) / kStripRows;
@@ -675,12 +680,12 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype) {
     for (;;) {
         const int64_t rows = (S + strips - 1) / strips;
         p.rows_per_strip = (rows + kRoundRows - 1) / kRoundRows * kRoundRows;
-        p.mask_lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + 2);
+        p.mask_lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + W - 1);
         if (p.mask_lds <= (size_t)kMaxMaskLds || strips >= max_strips) break;
         ++strips;  // keep the staged mask within its LDS budget
     }
     p.n_strips = (S + p.rows_per_strip - 1) / p.rows_per_strip;
-    p.ws_bytes = (uint64_t)p.n_strips * 3u * (uint64_t)p.C * sizeof(double);
+    p.ws_bytes = (uint64_t)p.n_strips * (uint64_t)W * (uint64_t)p.C * sizeof(double);
     return p;
 }
 
@@ -708,20 +713,29 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     const size_t lds_floor = MCCB_LDS_FLOOR;
     const size_t lds = mask ? (p.mask_lds > lds_floor ? p.mask_lds : lds_floor) : lds_floor;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
-#define MCCB_FUSED(M, T)                                                                          \
-    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T>), grid1, block1, lds, st, (const vec_t *)gy,     \
-                       (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx, (double *)ws, p.S,  \
-                       p.B, p.H, p.rows_per_strip, p.n_col_blocks, is)
-    if (mask) {
-        if (strided) MCCB_FUSED(true, true); else MCCB_FUSED(true, false);
-    } else {
-        if (strided) MCCB_FUSED(false, true); else MCCB_FUSED(false, false);
+#define MCCB_FUSED(M, T, TAPS)                                                                    \
+    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS>), grid1, block1, lds, st,                 \
+                       (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx,  \
+                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, p.n_col_blocks, is)
+#define MCCB_FUSED_W(TAPS)                                                                        \
+    if (mask) {                                                                                   \
+        if (strided) MCCB_FUSED(true, true, TAPS); else MCCB_FUSED(true, false, TAPS);            \
+    } else {                                                                                      \
+        if (strided) MCCB_FUSED(false, true, TAPS); else MCCB_FUSED(false, false, TAPS);          \
     }
+    switch (p.W) {
+        case 1: MCCB_FUSED_W(1); break;
+        case 2: MCCB_FUSED_W(2); break;
+        case 3: MCCB_FUSED_W(3); break;
+        case 4: MCCB_FUSED_W(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MCCB_FUSED_W
 #undef MCCB_FUSED
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hipErrorInvalidValue;
-    const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), 3);
+    const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
                        (uint32_t *)gw, p.n_strips, p.B, p.H);
@@ -743,20 +757,29 @@ FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
 }
 
 template <int DT>
-hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, const void *x, const void *w,
+hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, int W, const void *x, const void *w,
                       const uint8_t *mask, void *y, hipStream_t st, const InStrides &is,
                       bool strided) {
     const FwdPlan f = make_fwd_plan(S, B, H);
     const dim3 grid((unsigned)(f.n_ct * f.n_rt));
     const dim3 block(kFwdWaves * kWave);
-#define MCCB_FWD(M, T)                                                                            \
-    hipLaunchKernelGGL((mccb_fwd<DT, M, T>), grid, block, MCCB_FWD_LDS, st, (const fvec_t *)x,     \
-                       (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, is)
-    if (mask) {
-        if (strided) MCCB_FWD(true, true); else MCCB_FWD(true, false);
-    } else {
-        if (strided) MCCB_FWD(false, true); else MCCB_FWD(false, false);
+#define MCCB_FWD(M, T, TAPS)                                                                      \
+    hipLaunchKernelGGL((mccb_fwd<DT, M, T, TAPS>), grid, block, MCCB_FWD_LDS, st,                \
+                       (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, is)
+#define MCCB_FWD_W(TAPS)                                                                          \
+    if (mask) {                                                                                   \
+        if (strided) MCCB_FWD(true, true, TAPS); else MCCB_FWD(true, false, TAPS);                \
+    } else {                                                                                      \
+        if (strided) MCCB_FWD(false, true, TAPS); else MCCB_FWD(false, false, TAPS);              \
     }
+    switch (W) {
+        case 1: MCCB_FWD_W(1); break;
+        case 2: MCCB_FWD_W(2); break;
+        case 3: MCCB_FWD_W(3); break;
+        case 4: MCCB_FWD_W(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MCCB_FWD_W
 #undef MCCB_FWD
     return hipGetLastError();
 }
@@ -804,8 +827,9 @@ struct ExLayout {
 };
 
 // Workspace layout: `base` bytes of the kernels' own scratch, then the packed copies needed.
-ExLayout ex_layout(uint64_t base, int64_t S, int64_t B, int64_t H, const View3 *gy, const View3 &x,
-                   const void *w, int64_t w0, int64_t w1, int vec, uint64_t span_limit) {
+ExLayout ex_layout(uint64_t base, int64_t S, int64_t B, int64_t H, int64_t W, const View3 *gy,
+                   const View3 &x, const void *w, int64_t w0, int64_t w1, int vec,
+                   uint64_t span_limit) {
     ExLayout L;
     const uint64_t nb = (uint64_t)(S * B * H) * 2u;
     uint64_t off = base;
@@ -822,7 +846,7 @@ ExLayout ex_layout(uint64_t base, int64_t S, int64_t B, int64_t H, const View3 *
     if (!(w0 == H && w1 == 1 && ((uintptr_t)w & 15u) == 0)) {
         L.pack_w = true;
         L.w_off = off = align256(off);
-        off += (uint64_t)(3 * H) * 2u;
+        off += (uint64_t)(W * H) * 2u;
     }
     L.total = off;
     return L;
@@ -845,7 +869,7 @@ struct ExArgs {
 // Fills `a` from the strides (NULL = contiguous) and checks them: non-negative, element-aligned
 // bases, extents that fit. `gy` may be NULL (forward).
 int check_strided(const void *gy, const void *x, const void *w, const uint8_t *mask, int64_t S,
-                  int64_t B, int64_t H, const mccb_strides_t *sp, ExArgs &a) {
+                  int64_t B, int64_t H, int64_t W, const mccb_strides_t *sp, ExArgs &a) {
     const int64_t C = B * H;
     a.gy = View3{gy, C, H, 1};
     a.x = View3{x, C, H, 1};
@@ -862,7 +886,7 @@ int check_strided(const void *gy, const void *x, const void *w, const uint8_t *m
         return MCCB_ERR_PARAM_INVALID;
     a.gy_ext = gy ? extent_bytes(S, a.gy.s0, B, a.gy.s1, H, a.gy.s2, 2) : 0;
     a.x_ext = extent_bytes(S, a.x.s0, B, a.x.s1, H, a.x.s2, 2);
-    a.w_ext = extent_bytes(3, a.w0, 1, 0, H, a.w1, 2);
+    a.w_ext = extent_bytes(W, a.w0, 1, 0, H, a.w1, 2);
     a.m_ext = mask ? extent_bytes(B, a.m0, S, a.m1, 1, 0, 1) : 0;
     if ((gy && !a.gy_ext) || !a.x_ext || !a.w_ext || (mask && !a.m_ext)) return MCCB_ERR_PARAM_INVALID;
     return MCCB_OK;
@@ -968,42 +992,46 @@ int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y
     hipStream_t st = (hipStream_t)stream;
     const InStrides is{B * H, H, B * H, H, S, 1};
     const hipError_t e = (dtype == MCCB_BF16)
-                             ? launch_fwd<MCCB_BF16>(S, B, H, x, weight, mask, y, st, is, false)
-                             : launch_fwd<MCCB_FP16>(S, B, H, x, weight, mask, y, st, is, false);
+                             ? launch_fwd<MCCB_BF16>(S, B, H, 3, x, weight, mask, y, st, is, false)
+                             : launch_fwd<MCCB_FP16>(S, B, H, 3, x, weight, mask, y, st, is, false);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 
 int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *weight, int64_t S,
-                               int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
-                               uint64_t *workspace_size) {
+                               int64_t B, int64_t H, int64_t W, int dtype,
+                               const mccb_strides_t *strides, uint64_t *workspace_size) {
     if (!gradY || !x || !weight || !workspace_size) return MCCB_ERR_PARAM_NULLPTR;
     int rc = check_shape(S, B, H, dtype);
+    if (rc == MCCB_OK) rc = check_taps(W);
     if (rc != MCCB_OK) return rc;
     ExArgs a;
-    rc = check_strided(gradY, x, weight, nullptr, S, B, H, strides, a);
+    rc = check_strided(gradY, x, weight, nullptr, S, B, H, W, strides, a);
     if (rc != MCCB_OK) return rc;
-    const Plan p = make_plan(S, B, H, dtype);
-    *workspace_size = ex_layout(p.ws_bytes, S, B, H, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan).total;
+    const Plan p = make_plan(S, B, H, dtype, (int)W);
+    *workspace_size =
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan).total;
     return MCCB_OK;
 }
 
 int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
-                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
-                     const mccb_strides_t *strides, void *workspace, uint64_t workspace_size,
-                     void *stream) {
+                     void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int64_t W,
+                     int dtype, const mccb_strides_t *strides, void *workspace,
+                     uint64_t workspace_size, void *stream) {
     if (!gradY || !x || !weight || !gradX || !gradWeight) return MCCB_ERR_PARAM_NULLPTR;
     int rc = check_shape(S, B, H, dtype);
+    if (rc == MCCB_OK) rc = check_taps(W);
     if (rc != MCCB_OK) return rc;
     ExArgs a;
-    rc = check_strided(gradY, x, weight, mask, S, B, H, strides, a);
+    rc = check_strided(gradY, x, weight, mask, S, B, H, W, strides, a);
     if (rc != MCCB_OK) return rc;
-    const Plan p = make_plan(S, B, H, dtype);
-    const ExLayout L = ex_layout(p.ws_bytes, S, B, H, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan);
+    const Plan p = make_plan(S, B, H, dtype, (int)W);
+    const ExLayout L =
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan);
     if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
     if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
     if (!aligned16(gradX) || !aligned16(gradWeight) || (L.total > 0 && !aligned16(workspace)))
         return MCCB_ERR_PARAM_INVALID;
-    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(W * H) * 2u;
     const void *bufs[7] = {gradY, x, weight, mask, gradX, gradWeight, workspace};
     const uint64_t lens[7] = {a.gy_ext, a.x_ext, a.w_ext, a.m_ext, nb, wb, L.total};
     if (any_overlap(bufs, lens, 7, 4)) return MCCB_ERR_PARAM_INVALID;
@@ -1024,7 +1052,7 @@ int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const
         x_eff = wsb + L.x_off, is.x_row = C, is.x_batch = H;
     }
     if (L.pack_w) {
-        if (pack3(weight, wsb + L.w_off, 3, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
+        if (pack3(weight, wsb + L.w_off, W, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
             return MCCB_ERR_RUNTIME;
         w_eff = wsb + L.w_off;
     }
@@ -1044,28 +1072,30 @@ int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const
 }
 
 int mccb_forward_get_workspace_size_ex(const void *x, const void *weight, int64_t S, int64_t B,
-                                       int64_t H, int dtype, const mccb_strides_t *strides,
-                                       uint64_t *workspace_size) {
+                                       int64_t H, int64_t W, int dtype,
+                                       const mccb_strides_t *strides, uint64_t *workspace_size) {
     if (!x || !weight || !workspace_size) return MCCB_ERR_PARAM_NULLPTR;
     int rc = check_shape(S, B, H, dtype);
+    if (rc == MCCB_OK) rc = check_taps(W);
     if (rc != MCCB_OK) return rc;
     ExArgs a;
-    rc = check_strided(nullptr, x, weight, nullptr, S, B, H, strides, a);
+    rc = check_strided(nullptr, x, weight, nullptr, S, B, H, W, strides, a);
     if (rc != MCCB_OK) return rc;
-    *workspace_size = ex_layout(0, S, B, H, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0).total;
+    *workspace_size = ex_layout(0, S, B, H, W, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0).total;
     return MCCB_OK;
 }
 
 int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
-                    int64_t B, int64_t H, int dtype, const mccb_strides_t *strides,
+                    int64_t B, int64_t H, int64_t W, int dtype, const mccb_strides_t *strides,
                     void *workspace, uint64_t workspace_size, void *stream) {
     if (!x || !weight || !y) return MCCB_ERR_PARAM_NULLPTR;
     int rc = check_shape(S, B, H, dtype);
+    if (rc == MCCB_OK) rc = check_taps(W);
     if (rc != MCCB_OK) return rc;
     ExArgs a;
-    rc = check_strided(nullptr, x, weight, mask, S, B, H, strides, a);
+    rc = check_strided(nullptr, x, weight, mask, S, B, H, W, strides, a);
     if (rc != MCCB_OK) return rc;
-    const ExLayout L = ex_layout(0, S, B, H, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0);
+    const ExLayout L = ex_layout(0, S, B, H, W, nullptr, a.x, weight, a.w0, a.w1, kFwdVec, 0);
     if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
     if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
     if (!aligned16(y) || (L.total > 0 && !aligned16(workspace))) return MCCB_ERR_PARAM_INVALID;
@@ -1085,15 +1115,15 @@ int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void
         x_eff = wsb + L.x_off, is.x_row = C, is.x_batch = H;
     }
     if (L.pack_w) {
-        if (pack3(weight, wsb + L.w_off, 3, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
+        if (pack3(weight, wsb + L.w_off, W, 1, H, a.w0, 0, a.w1, st) != hipSuccess)
             return MCCB_ERR_RUNTIME;
         w_eff = wsb + L.w_off;
     }
     const bool strided = !(is.x_row == C && is.x_batch == H);
     const hipError_t e =
         (dtype == MCCB_BF16)
-            ? launch_fwd<MCCB_BF16>(S, B, H, x_eff, w_eff, mask, y, st, is, strided)
-            : launch_fwd<MCCB_FP16>(S, B, H, x_eff, w_eff, mask, y, st, is, strided);
+            ? launch_fwd<MCCB_BF16>(S, B, H, (int)W, x_eff, w_eff, mask, y, st, is, strided)
+            : launch_fwd<MCCB_FP16>(S, B, H, (int)W, x_eff, w_eff, mask, y, st, is, strided);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 

@@ -55,6 +55,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_backward.restype = ctypes.c_int
     lib.oracle_forward.argtypes = [i64, i64, i64, _f64p, _f64p, _u8p, _f64p]
     lib.oracle_forward.restype = ctypes.c_int
+    lib.oracle_backward_w.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, _u16p, _u16p,
+                                      _u16p, _u8p, _f64p, _u16p, _f64p, _f64p, _u16p]
+    lib.oracle_backward_w.restype = ctypes.c_int
+    lib.oracle_forward_w.argtypes = [ctypes.c_int, i64, i64, i64, _f64p, _f64p, _u8p, _f64p]
+    lib.oracle_forward_w.restype = ctypes.c_int
     return lib
 
 
@@ -92,10 +97,11 @@ class Oracle:
     # -- the backward -----------------------------------------------------------------------------
     def backward(self, dtype: str, gY: np.ndarray, x: np.ndarray, w: np.ndarray,
                  mask: np.ndarray | None, want_gx64: bool = True) -> dict:
-        """gY, x: uint16 [S,B,H]; w: uint16 [3,H]; mask: uint8/bool [B,S] or None.
+        """gY, x: uint16 [S,B,H]; w: uint16 [W,H] (the window W is w's first dimension, 3 on the
+        page); mask: uint8/bool [B,S] or None.
 
         Returns a dict with ``gx16`` (uint16 [S,B,H]), ``gx64`` (float64 [S,B,H], if asked),
-        ``gw16`` (uint16 [3,H]), ``gw64`` (float64 [3,H]) and ``gwrss`` (float64 [3,H]).
+        ``gw16`` (uint16 [W,H]), ``gw64`` (float64 [W,H]) and ``gwrss`` (float64 [W,H]).
         """
         gY = np.ascontiguousarray(gY, dtype=np.uint16)
         x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -103,8 +109,9 @@ class Oracle:
         if gY.ndim != 3 or x.shape != gY.shape:
             raise ValueError("gY and x must both be [S,B,H]")
         S, B, H = gY.shape
-        if w.shape != (3, H):
-            raise ValueError("w must be [3,H]")
+        if w.ndim != 2 or w.shape[1] != H or w.shape[0] < 1:
+            raise ValueError("w must be [W,H]")
+        W = int(w.shape[0])
         m = None
         if mask is not None:
             m = np.ascontiguousarray(mask).astype(np.uint8, copy=False)
@@ -112,14 +119,14 @@ class Oracle:
                 raise ValueError("mask must be [B,S]")
         out = {
             "gx16": np.empty((S, B, H), dtype=np.uint16),
-            "gw16": np.empty((3, H), dtype=np.uint16),
-            "gw64": np.empty((3, H), dtype=np.float64),
-            "gwrss": np.empty((3, H), dtype=np.float64),
+            "gw16": np.empty((W, H), dtype=np.uint16),
+            "gw64": np.empty((W, H), dtype=np.float64),
+            "gwrss": np.empty((W, H), dtype=np.float64),
         }
         if want_gx64:
             out["gx64"] = np.empty((S, B, H), dtype=np.float64)
-        rc = self.lib.oracle_backward(
-            DTYPE_CODE[dtype], S, B, H, _ptr(gY, _u16p), _ptr(x, _u16p), _ptr(w, _u16p),
+        rc = self.lib.oracle_backward_w(
+            DTYPE_CODE[dtype], W, S, B, H, _ptr(gY, _u16p), _ptr(x, _u16p), _ptr(w, _u16p),
             None if m is None else _ptr(m, _u8p),
             _ptr(out["gx64"], _f64p) if want_gx64 else None, _ptr(out["gx16"], _u16p),
             _ptr(out["gw64"], _f64p), _ptr(out["gwrss"], _f64p), _ptr(out["gw16"], _u16p))
@@ -128,14 +135,18 @@ class Oracle:
         return out
 
     def forward(self, x64: np.ndarray, w64: np.ndarray, mask: np.ndarray | None) -> np.ndarray:
-        """fp64 causal depthwise forward y = mask * conv(x, w); used by the adjoint test."""
+        """fp64 causal depthwise forward y = mask * conv(x, w), w [W,H]; used by the adjoint test
+        and, rounded by forward16, as the forward's reference."""
         x64 = np.ascontiguousarray(x64, dtype=np.float64)
         w64 = np.ascontiguousarray(w64, dtype=np.float64)
         S, B, H = x64.shape
+        if w64.ndim != 2 or w64.shape[1] != H or w64.shape[0] < 1:
+            raise ValueError("w must be [W,H]")
         m = None if mask is None else np.ascontiguousarray(mask).astype(np.uint8, copy=False)
         y = np.empty_like(x64)
-        rc = self.lib.oracle_forward(S, B, H, _ptr(x64, _f64p), _ptr(w64, _f64p),
-                                     None if m is None else _ptr(m, _u8p), _ptr(y, _f64p))
+        rc = self.lib.oracle_forward_w(int(w64.shape[0]), S, B, H, _ptr(x64, _f64p),
+                                       _ptr(w64, _f64p), None if m is None else _ptr(m, _u8p),
+                                       _ptr(y, _f64p))
         if rc != 0:
             raise RuntimeError(f"oracle_forward failed ({rc})")
         return y

@@ -17,7 +17,9 @@
  *     mask is an optional bool [B,S]; the float tensors are BFLOAT16 or FLOAT16.
  *   - section 约束说明 (constraints): B in 1..32, B*S in 1..512K, H in 384..24576 and a multiple of
  *     64, W = 3. The oracle does NOT enforce these limits: it is the definition and accepts any
- *     positive S, B, H so that tiny hand-worked cases can be checked.
+ *     positive S, B, H so that tiny hand-worked cases can be checked. The *_w entry points take the
+ *     window W as written in the equations (any W >= 1; the page's is 3), for the kernels' W != 3
+ *     extension.
  *
  * Readings where the page is silent (the same readings the library documents):
  *   - mask "true" keeps the gradient (the equation multiplies by it); a null mask means all-true
@@ -46,7 +48,7 @@
 
 #define OR_BF16 0
 #define OR_FP16 1
-#define OR_TAPS 3 /* W: the constraints section fixes the window at 3 */
+#define OR_TAPS 3 /* W: the constraints section fixes the window at 3 (for now) */
 
 /* ------------------------------------------------------------------------------------------------
  * Codec, written from the IEEE 754 binary16 layout (1 sign, 5 exponent, 10 fraction bits, bias 15)
@@ -149,13 +151,12 @@ static double grad_y_masked(const double *gy, const uint8_t *mask, int64_t S, in
  *   gwrss [3,H]   sqrt(sum of the squared gradWeight terms), a scale for the gradWeight tolerance
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_backward(int dtype, int64_t S, int64_t B, int64_t H, const uint16_t *gY,
-                    const uint16_t *x, const uint16_t *w, const uint8_t *mask, double *gx64,
-                    uint16_t *gx16, double *gw64, double *gwrss, uint16_t *gw16) {
-    if (S < 1 || B < 1 || H < 1 || !gY || !x || !w) return -1;
+int oracle_backward_w(int dtype, int W, int64_t S, int64_t B, int64_t H, const uint16_t *gY,
+                      const uint16_t *x, const uint16_t *w, const uint8_t *mask, double *gx64,
+                      uint16_t *gx16, double *gw64, double *gwrss, uint16_t *gw16) {
+    if (S < 1 || B < 1 || H < 1 || W < 1 || !gY || !x || !w) return -1;
     if (dtype != OR_BF16 && dtype != OR_FP16) return -1;
     const int64_t N = S * B * H;
-    const int W = OR_TAPS;
     double *gyd = (double *)malloc(sizeof(double) * (size_t)N);
     double *xd = (double *)malloc(sizeof(double) * (size_t)N);
     double *wd = (double *)malloc(sizeof(double) * (size_t)(W * H));
@@ -207,16 +208,23 @@ int oracle_backward(int dtype, int64_t S, int64_t B, int64_t H, const uint16_t *
     return 0;
 }
 
+/* The page's window, W = 3. */
+int oracle_backward(int dtype, int64_t S, int64_t B, int64_t H, const uint16_t *gY,
+                    const uint16_t *x, const uint16_t *w, const uint8_t *mask, double *gx64,
+                    uint16_t *gx16, double *gw64, double *gwrss, uint16_t *gw16) {
+    return oracle_backward_w(dtype, OR_TAPS, S, B, H, gY, x, w, mask, gx64, gx16, gw64, gwrss,
+                             gw16);
+}
+
 /*
  * The forward that these gradients belong to, used only by the adjoint (dot-product) test. The
  * page prints only the backward; the forward is the causal depthwise convolution whose adjoint the
  * equations are: y[i,j] = mask[j,i] * sum_{k=0}^{W-1} weight[k] * x[i-(W-1)+k, j], x[<0] = 0.
- * Operates on fp64 arrays (x [S,B,H], w [3,H], y [S,B,H]).
+ * Operates on fp64 arrays (x [S,B,H], w [W,H], y [S,B,H]).
  */
-int oracle_forward(int64_t S, int64_t B, int64_t H, const double *x, const double *w,
-                   const uint8_t *mask, double *y) {
-    if (S < 1 || B < 1 || H < 1 || !x || !w || !y) return -1;
-    const int W = OR_TAPS;
+int oracle_forward_w(int W, int64_t S, int64_t B, int64_t H, const double *x, const double *w,
+                     const uint8_t *mask, double *y) {
+    if (S < 1 || B < 1 || H < 1 || W < 1 || !x || !w || !y) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t h = 0; h < H; ++h) {
         for (int64_t i = 0; i < S; ++i) {
@@ -233,4 +241,10 @@ int oracle_forward(int64_t S, int64_t B, int64_t H, const double *x, const doubl
         }
     }
     return 0;
+}
+
+/* The page's window, W = 3. */
+int oracle_forward(int64_t S, int64_t B, int64_t H, const double *x, const double *w,
+                   const uint8_t *mask, double *y) {
+    return oracle_forward_w(OR_TAPS, S, B, H, x, w, mask, y);
 }

@@ -30,6 +30,7 @@ class Workload:
     w: tuple  # distribution of weight
     mask: tuple  # ("bernoulli", p) | ("prefix",) | ("all_true",) | ("null",)
     seed: int
+    W: int = 3  # window taps: weight and gradWeight are [W,H]
 
     @property
     def N(self) -> int:
@@ -41,15 +42,15 @@ class Workload:
 
     def algorithmic_bytes(self) -> int:
         """Bytes the method must move: read gradY and x, write gradX (2 bytes each per element),
-        read the mask (1 byte per (j,i)) if present, read weight and write gradWeight [3,H]."""
+        read the mask (1 byte per (j,i)) if present, read weight and write gradWeight [W,H]."""
         e = 2
-        return 3 * self.N * e + (self.B * self.S if self.has_mask else 0) + 2 * 3 * self.H * e
+        return 3 * self.N * e + (self.B * self.S if self.has_mask else 0) + 2 * self.W * self.H * e
 
     def describe(self) -> str:
         m = {"bernoulli": f"mask Bernoulli({self.mask[1] if len(self.mask) > 1 else ''})",
              "prefix": "mask per-batch valid prefix, length uniform in [S/2,S]",
              "all_true": "mask all-true", "null": "mask null (all-true)"}[self.mask[0]]
-        return f"S={self.S} B={self.B} H={self.H} W=3 {self.dtype}, {m}"
+        return f"S={self.S} B={self.B} H={self.H} W={self.W} {self.dtype}, {m}"
 
 
 def _w(i, name, S, B, H, dtype, gy, x, w, mask):
@@ -73,9 +74,16 @@ HEADLINE = 3  # B*S = 512K, H = 5120
 
 
 def custom(S: int, B: int, H: int, dtype: str = "bf16", mask: tuple = ("bernoulli", 0.8),
-           seed: int = 7, gy=("normal", 1.0), x=("normal", 1.0), w=("normal", 0.5)) -> Workload:
+           seed: int = 7, gy=("normal", 1.0), x=("normal", 1.0), w=("normal", 0.5),
+           W: int = 3) -> Workload:
     """An ad-hoc workload (edge shapes in the tests)."""
-    return Workload(f"S{S}_B{B}_H{H}_{dtype}", S, B, H, dtype, gy, x, w, mask, seed)
+    name = f"S{S}_B{B}_H{H}_{dtype}" + ("" if W == 3 else f"_W{W}")
+    return Workload(name, S, B, H, dtype, gy, x, w, mask, seed, W)
+
+
+def with_taps(wl: Workload, W: int) -> Workload:
+    """The same workload with a W-tap window (its weight stream extended or cut to [W,H])."""
+    return dataclasses.replace(wl, name=f"{wl.name}_W{W}" if W != 3 else wl.name, W=W)
 
 
 # -- generation -------------------------------------------------------------------------------------
@@ -109,8 +117,8 @@ def prefix_lengths(wl: Workload) -> torch.Tensor:
 
 
 def weight_tensor(wl: Workload, device="cpu") -> torch.Tensor:
-    idx = torch.arange(3 * wl.H, dtype=torch.int64)
-    return gen.values_at(key(wl, STREAM_W), idx, wl.dtype, wl.w).view(3, wl.H).to(device)
+    idx = torch.arange(wl.W * wl.H, dtype=torch.int64)
+    return gen.values_at(key(wl, STREAM_W), idx, wl.dtype, wl.w).view(wl.W, wl.H).to(device)
 
 
 def full_tensor(wl: Workload, stream: int, device) -> torch.Tensor:

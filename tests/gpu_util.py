@@ -43,12 +43,22 @@ def gpu_inputs(wl, device="cuda"):
     return gy, x, w, m
 
 
+def workspace_for(wl, gy, x, w):
+    """Workspace of the call the binding makes for these tensors (plain or extended)."""
+    if wl.W == 3:
+        return mdc.workspace_for(wl.S, wl.B, wl.H, gy.dtype, gy.device)
+    n = mdc.mccb_get_workspace_size_ex(gy.data_ptr(), x.data_ptr(), w.data_ptr(), wl.S, wl.B,
+                                       wl.H, wl.W, mdc.DTYPE_CODE[gy.dtype], None)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=gy.device)
+
+
 def gpu_run(wl, inputs=None, device="cuda", poison_workspace=False):
     gy, x, w, m = inputs if inputs is not None else gpu_inputs(wl, device)
-    ws = mdc.workspace_for(wl.S, wl.B, wl.H, gy.dtype, gy.device)
+    ws = workspace_for(wl, gy, x, w)
     if poison_workspace:
         ws.fill_(0xFF)
-    announce(f"mccb_backward {wl.name} S={wl.S} B={wl.B} H={wl.H} {wl.dtype} mask={wl.mask[0]}")
+    announce(f"mccb_backward {wl.name} S={wl.S} B={wl.B} H={wl.H} W={wl.W} {wl.dtype} "
+             f"mask={wl.mask[0]}")
     gx, gw = mdc.backward(gy, x, w, m, workspace=ws)
     torch.cuda.synchronize()
     return gx, gw
@@ -125,14 +135,14 @@ def compare_columns(wl, gx, gw, hs: np.ndarray, tag=None):
 
 
 def compare_rows(wl, gx, rows: np.ndarray, tag=None):
-    """Exact check of whole gradX rows: row i depends only on gradY rows i..i+2 and the mask there,
-    so the oracle runs on that 3-row (or shorter, at the end) slab."""
+    """Exact check of whole gradX rows: row i depends only on gradY rows i..i+W-1 and the mask
+    there, so the oracle runs on that W-row (or shorter, at the end) slab."""
     tag = tag or wl.name
     m = wls.mask_tensor(wl, "cpu")
     w = wls.bits(wls.weight_tensor(wl, "cpu"))
     for r in rows:
         r = int(r)
-        rr = torch.arange(r, min(r + 3, wl.S), dtype=torch.int64)
+        rr = torch.arange(r, min(r + wl.W, wl.S), dtype=torch.int64)
         gy_r = wls.bits(wls.row_tensor(wl, wls.STREAM_GY, rr))
         x_r = wls.bits(wls.row_tensor(wl, wls.STREAM_X, rr))
         m_r = None if m is None else m[:, r:r + len(rr)].numpy()

@@ -208,17 +208,17 @@ def strides(S=64, B=2, H=384, gy=None, x=None, w=None, m=None):
     return st
 
 
-def xcall(gy=GY, x=X, w=W, m=M, gx=GX, gw=GW, S=64, B=2, H=384, dt=BF16, st=None, ws=WS,
+def xcall(gy=GY, x=X, w=W, m=M, gx=GX, gw=GW, S=64, B=2, H=384, taps=3, dt=BF16, st=None, ws=WS,
           wsz=1 << 40):
-    rc = mdc.mccb_backward_ex(gy, x, w, m, gx, gw, S, B, H, dt, st, ws, wsz, None)
+    rc = mdc.mccb_backward_ex(gy, x, w, m, gx, gw, S, B, H, taps, dt, st, ws, wsz, None)
     assert rc in VALIDATION_CODES, f"strided call passed validation with fake pointers (rc={rc})"
     return rc
 
 
 def test_ex_null_strides_is_the_contiguous_layout():
-    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, None) == _ws(64, 2, 384)
-    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, strides()) == _ws(64, 2, 384)
-    assert mdc.mccb_forward_get_workspace_size_ex(X, W, 64, 2, 384, BF16, None) == 0
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, 3, BF16, None) == _ws(64, 2, 384)
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, 3, BF16, strides()) == _ws(64, 2, 384)
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, 64, 2, 384, 3, BF16, None) == 0
 
 
 def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
@@ -226,20 +226,20 @@ def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
     base, nb = _ws(S, B, H), S * B * H * 2
     # [B,S,H] storage viewed as [S,B,H]: channels contiguous, strides even -> read in place
     perm = [H, S * H, 1]
-    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, strides(gy=perm, x=perm)) == base
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 3, BF16, strides(gy=perm, x=perm)) == base
     # channels strided -> gradY packed after the 256-aligned partials
     st = strides(gy=[B * H * 2, H * 2, 2])
-    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, st) == -(-base // 256) * 256 + nb
+    assert mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 3, BF16, st) == -(-base // 256) * 256 + nb
     # a base that is only 2-byte aligned cannot feed 4-byte lane loads -> x packed
-    assert mdc.mccb_get_workspace_size_ex(GY, X + 2, W, S, B, H, BF16, None) == \
+    assert mdc.mccb_get_workspace_size_ex(GY, X + 2, W, S, B, H, 3, BF16, None) == \
         -(-base // 256) * 256 + nb
     # a transposed weight is packed (3*H elements)
-    got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, BF16, strides(w=[1, 3]))
+    got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 3, BF16, strides(w=[1, 3]))
     assert got == -(-base // 256) * 256 + 3 * H * 2
     # forward: in place needs row/batch strides that are multiples of 8 and a 16-byte base
-    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, BF16, strides(x=perm)) == 0
-    assert mdc.mccb_forward_get_workspace_size_ex(X + 8, W, S, B, H, BF16, None) == nb
-    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, BF16,
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, 3, BF16, strides(x=perm)) == 0
+    assert mdc.mccb_forward_get_workspace_size_ex(X + 8, W, S, B, H, 3, BF16, None) == nb
+    assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, 3, BF16,
                                                   strides(x=[B * H + 2, H, 1])) == nb
 
 
@@ -256,7 +256,7 @@ def test_ex_negative_stride(field, idx):
     assert xcall(st=st) == INVALID
     if field != "mask":
         with pytest.raises(mdc.MccbError):
-            mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, st)
+            mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, 3, BF16, st)
 
 
 def test_ex_element_misaligned_input():
@@ -280,16 +280,18 @@ def test_ex_outputs_must_not_overlap_strided_extents():
 
 
 def test_ex_workspace_too_small():
-    need = mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, BF16, strides(gy=[768, 384, 2]))
+    need = mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, 3, BF16, strides(gy=[768, 384, 2]))
     assert xcall(st=strides(gy=[768, 384, 2]), wsz=need - 1) == INVALID
 
 
 def test_forward_ex_validation():
     def f(**kw):
-        args = dict(x=X, w=W, m=M, y=GX, S=64, B=2, H=384, dt=BF16, st=None, ws=WS, wsz=1 << 40)
+        args = dict(x=X, w=W, m=M, y=GX, S=64, B=2, H=384, taps=3, dt=BF16, st=None, ws=WS,
+                    wsz=1 << 40)
         args.update(kw)
         rc = mdc.mccb_forward_ex(args["x"], args["w"], args["m"], args["y"], args["S"], args["B"],
-                                 args["H"], args["dt"], args["st"], args["ws"], args["wsz"], None)
+                                 args["H"], args["taps"], args["dt"], args["st"], args["ws"],
+                                 args["wsz"], None)
         assert rc in VALIDATION_CODES, f"strided forward passed validation (rc={rc})"
         return rc
     assert f(x=None) == NULLPTR
@@ -299,3 +301,30 @@ def test_forward_ex_validation():
     assert f(y=GX + 8) == INVALID  # output stays 16-byte aligned
     assert f(x=X + 2, ws=None) == NULLPTR  # packing needed, no workspace
     assert f(S=0) == SHAPE
+    assert f(taps=0) == SHAPE
+    assert f(taps=5) == SHAPE
+
+
+# -- window taps W (mccb_*_ex) ----------------------------------------------------------------
+@pytest.mark.parametrize("taps", [0, -1, 5, 64])
+def test_ex_taps_out_of_range(taps):
+    assert xcall(taps=taps) == SHAPE
+    with pytest.raises(mdc.MccbError) as e:
+        mdc.mccb_get_workspace_size_ex(GY, X, W, 64, 2, 384, taps, BF16, None)
+    assert e.value.status == SHAPE
+
+
+@pytest.mark.parametrize("taps", [1, 2, 3, 4])
+def test_ex_workspace_scales_with_taps(taps):
+    # fp64 partials [n_strips][W][B*H]; the strips do not depend on W
+    for (S, B, H) in [(64, 2, 384), (16384, 32, 5120), (262144, 2, 24576)]:
+        p = mdc.mccb_get_plan(S, B, H, BF16)
+        got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, taps, BF16, None)
+        assert got == p["n_strips"] * taps * B * H * 8
+
+
+def test_ex_weight_extent_follows_taps():
+    # a [4,H] weight reaches 4*H elements: an output placed right after 3*H of them overlaps
+    H = 384
+    assert xcall(taps=4, gw=W + 3 * H * 2 + 256 - (3 * H * 2) % 256) == INVALID
+    assert xcall(taps=4, gx=W + 3 * H * 2) == INVALID

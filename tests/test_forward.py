@@ -35,7 +35,8 @@ def gpu_forward(wl, inputs=None, poison=False):
     y = torch.empty_like(x)
     if poison:
         y.view(torch.int16).fill_(0x7F80 if wl.dtype == "bf16" else 0x7C00)  # +inf everywhere
-    announce(f"mccb_forward {wl.name} S={wl.S} B={wl.B} H={wl.H} {wl.dtype} mask={wl.mask[0]}")
+    announce(f"mccb_forward {wl.name} S={wl.S} B={wl.B} H={wl.H} W={wl.W} {wl.dtype} "
+             f"mask={wl.mask[0]}")
     mdc.forward(x, w, m, y=y)
     torch.cuda.synchronize()
     return y
@@ -62,12 +63,12 @@ def compare_columns(wl, y, hs, tag=None):
 
 
 def compare_rows(wl, y, rows, tag=None):
-    """Whole output rows: row i depends on x rows i-2..i (fewer at the start) and mask row i."""
+    """Whole output rows: row i depends on x rows i-W+1..i (fewer at the start) and mask row i."""
     m = wls.mask_tensor(wl, "cpu")
     w = wls.bits(wls.weight_tensor(wl, "cpu"))
     for r in rows:
         r = int(r)
-        lo = max(r - 2, 0)
+        lo = max(r - (wl.W - 1), 0)
         rr = torch.arange(lo, r + 1, dtype=torch.int64)
         x_r = wls.bits(wls.row_tensor(wl, wls.STREAM_X, rr))
         m_r = None if m is None else m[:, lo:r + 1].contiguous()

@@ -61,11 +61,13 @@ def random_case(S, B, H, dtype="bf16", mask=("bernoulli", 0.7), seed=3):
 
 
 def torch_autograd(gy64, x64, w64, mask):
-    """Gradients of y = mask * causal_depthwise_conv1d(x, w) by PyTorch CPU fp64 autograd."""
+    """Gradients of y = mask * causal_depthwise_conv1d(x, w) by PyTorch CPU fp64 autograd; the
+    window W is w64's first dimension."""
     S, B, H = x64.shape
+    W = w64.shape[0]
     xt = torch.from_numpy(x64).permute(1, 2, 0).contiguous().requires_grad_(True)  # [B,H,S]
-    wt = torch.from_numpy(w64).t().contiguous().unsqueeze(1).requires_grad_(True)  # [H,1,3]
-    y = F.conv1d(xt, wt, padding=2, groups=H)[..., :S]
+    wt = torch.from_numpy(w64).t().contiguous().unsqueeze(1).requires_grad_(True)  # [H,1,W]
+    y = F.conv1d(xt, wt, padding=W - 1, groups=H)[..., :S]
     if mask is not None:
         y = y * torch.from_numpy(mask.astype(np.float64))[:, None, :]
     y.backward(torch.from_numpy(gy64).permute(1, 2, 0).contiguous())
@@ -112,6 +114,56 @@ def pin_forward_hand_cases(orc):
             tag = f"{c['name']}/{dtype}"
             assert np.array_equal(r["y64"], exp), (tag, r["y64"], exp)
             assert np.array_equal(from_bits(r["y16"], dtype), exp), tag
+
+
+WIN_GOLDEN = os.path.join(HERE, "golden", "window_hand_cases.json")
+
+
+def pin_window_hand_cases(orc):
+    for c in json.load(open(WIN_GOLDEN))["cases"]:
+        for dtype in ("bf16", "fp16"):
+            tag = f"{c['name']}/{dtype}"
+            m = None if c["mask"] is None else np.array(c["mask"], dtype=np.uint8)
+            x, w = to_bits(c["x"], dtype), to_bits(c["w"], dtype)
+            assert w.shape[0] == c["W"], tag
+            if c["op"] == "forward":
+                r = orc.forward16(dtype, x, w, m)
+                exp = np.array(c["y"], dtype=np.float64)
+                assert np.array_equal(r["y64"], exp), (tag, r["y64"], exp)
+                assert np.array_equal(from_bits(r["y16"], dtype), exp), tag
+                continue
+            r = orc.backward(dtype, to_bits(c["gY"], dtype), x, w, m)
+            exp_gx, exp_gw = np.array(c["gX"], np.float64), np.array(c["gW"], np.float64)
+            assert np.array_equal(r["gx64"], exp_gx), (tag, r["gx64"], exp_gx)
+            assert np.array_equal(r["gw64"], exp_gw), (tag, r["gw64"], exp_gw)
+            assert np.array_equal(from_bits(r["gx16"], dtype), exp_gx), tag
+            assert np.array_equal(from_bits(r["gw16"], dtype), exp_gw), tag
+            np.testing.assert_allclose(r["gwrss"] ** 2, np.array(c["gW_sumsq"], float),
+                                       rtol=1e-12, err_msg=tag)
+
+
+def pin_window_autograd_and_adjoint(orc):
+    """W != 3 against PyTorch autograd of conv1d(kernel W, padding W-1) and the adjoint
+    identity <F(x,w), gY> = <x, gradX> = <w, gradWeight>."""
+    for W in (1, 2, 4):
+        for n, (S, B, H) in enumerate(SHAPES):
+            wl = synth.custom(S, B, H, "bf16", ("bernoulli", 0.7), seed=130 + n, W=W)
+            inp = wls.host_inputs(wl)
+            gy, x, w = wls.bits(inp["gy"]), wls.bits(inp["x"]), wls.bits(inp["w"])
+            m = None if inp["mask"] is None else inp["mask"].numpy()
+            assert w.shape == (W, H)
+            gy64, x64, w64 = (from_bits(a, "bf16") for a in (gy, x, w))
+            r = orc.backward("bf16", gy, x, w, m)
+            gx_ref, gw_ref = torch_autograd(gy64, x64, w64, m)
+            sx = max(1.0, float(np.abs(gx_ref).max()))
+            assert np.allclose(r["gx64"], gx_ref, rtol=0, atol=1e-13 * sx), (W, S, B, H)
+            sw = max(1.0, float(np.abs(gw_ref).max()))
+            assert np.allclose(r["gw64"], gw_ref, rtol=0, atol=1e-12 * sw), (W, S, B, H)
+            y = orc.forward(x64, w64, m)
+            lhs, mid = float(np.sum(y * gy64)), float(np.sum(x64 * r["gx64"]))
+            rhs = float(np.sum(w64 * r["gw64"]))
+            scale = float(np.sum(np.abs(y * gy64))) + 1e-300
+            assert abs(lhs - mid) <= 1e-12 * scale and abs(lhs - rhs) <= 1e-12 * scale, (W, S)
 
 
 def pin_call_example(orc):
@@ -298,7 +350,8 @@ def pin_codec_encode_bf16(orc):
     assert np.all(same | zero)
 
 
-PINS = [pin_hand_cases, pin_forward_hand_cases, pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
+PINS = [pin_hand_cases, pin_forward_hand_cases, pin_window_hand_cases,
+        pin_window_autograd_and_adjoint, pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
         pin_codec_decode, pin_codec_roundtrip, pin_codec_encode_fp16, pin_codec_encode_bf16]
 
 
@@ -354,6 +407,12 @@ MUTANTS = [
     ("forward shifted one row back", "const int64_t src = i - (W - 1) + k;",
      "const int64_t src = i - W + k;"),
     ("forward ignores the mask", "y[(i * B + j) * H + h] = m * acc;", "y[(i * B + j) * H + h] = acc;"),
+    ("gradX window stuck at 3 taps",
+     "for (int k = 0; k < W; ++k) {\n                    acc += grad_y_masked",
+     "for (int k = 0; k < W && k < 3; ++k) {\n                    acc += grad_y_masked"),
+    ("forward window stuck at 3 taps",
+     "for (int k = 0; k < W; ++k) {\n                    const int64_t src",
+     "for (int k = 0; k < W && k < 3; ++k) {\n                    const int64_t src"),
 ]
 
 
