@@ -10,8 +10,9 @@ bytes the method must move: read gradY and x, write gradX (2 bytes each per elem
 The same run also times the forward (mccb_forward, y = mask * causal conv(x, w)) on the same x,
 weight and mask, reported in the "forward" object of the same line: effective GB/s over its
 algorithmic bytes (read x, write y, read the mask and the weight); and both ops again on the same
-values stored [B,S,H] and passed as strided [S,B,H] views ("strided" object), and with 2- and
-4-tap windows instead of the page's 3 ("taps" object).
+values stored [B,S,H] and passed as strided [S,B,H] views ("strided" object), with 2- and 4-tap
+windows instead of the page's 3 ("taps" object), and on the workload's valid tokens packed into
+the variable-length layout ("varlen" object).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -125,6 +126,8 @@ def main() -> int:
                     help="skip timing both ops on [B,S,H]-stored (strided) inputs")
     ap.add_argument("--no-taps", action="store_true",
                     help="skip timing both ops with 2- and 4-tap windows")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip timing both ops on the packed variable-length layout")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -285,6 +288,48 @@ def main() -> int:
             del ww, gww, ws_w, y
         torch.cuda.empty_cache()
 
+    varlen = None
+    if not args.no_varlen:
+        # the workload's tokens packed: one sequence per batch, lengths uniform in [S/2, S]
+        lengths = wls.varlen_lengths(wl)
+        T = int(lengths.sum())
+        gy_v, x_v = wls.pack_tokens(gy, lengths), wls.pack_tokens(x, lengths)
+        cu = wls.cu_seqlens(lengths, dev)
+        gx_v, gw_v, y_v = torch.empty_like(gy_v), torch.empty_like(w), torch.empty_like(x_v)
+        ws_b = torch.empty(mdc.mccb_varlen_get_workspace_size(T, wl.B, wl.H, 3,
+                                                              mdc.DTYPE_CODE[gy.dtype]),
+                           dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(mdc.mccb_varlen_forward_get_workspace_size(T, wl.B, wl.H, 3,
+                                                                      mdc.DTYPE_CODE[gy.dtype]),
+                           dtype=torch.uint8, device=dev)
+
+        def timed_v(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / args.steps
+
+        b_ms = timed_v(lambda: mdc.varlen_backward(gy_v, x_v, w, cu, None, gradX=gx_v,
+                                                   gradWeight=gw_v, workspace=ws_b, stream=stream))
+        f_ms = timed_v(lambda: mdc.varlen_forward(x_v, w, cu, None, y=y_v, workspace=ws_f,
+                                                  stream=stream))
+        b_alg = 6 * T * wl.H + 2 * 3 * wl.H * 2 + 8 * wl.B
+        f_alg = 4 * T * wl.H + 3 * wl.H * 2 + 8 * wl.B
+        varlen = {"layout": f"packed [T,H], T={T} tokens in {wl.B} sequences (lengths uniform in "
+                            f"[S/2, S]), H={wl.H}, no mask",
+                  "backward": {"value": round(b_alg / (b_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "ms_per_step": round(b_ms, 5), "algorithmic_bytes": b_alg},
+                  "forward": {"value": round(f_alg / (f_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "ms_per_step": round(f_ms, 5), "algorithmic_bytes": f_alg}}
+        log(f"varlen T={T}: backward {b_ms:.4f} ms, forward {f_ms:.4f} ms")
+        del gy_v, x_v, gx_v, gw_v, y_v, ws_b, ws_f
+        torch.cuda.empty_cache()
+
     ceiling = None
     if not args.no_ceiling:
         ceiling = round(copy_ceiling(torch, dev), 1)
@@ -317,6 +362,7 @@ def main() -> int:
         "forward": fwd,
         "strided": strided,
         "taps": taps,
+        "varlen": varlen,
     }
     print(json.dumps(out), flush=True)
     return 0

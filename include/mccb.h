@@ -173,6 +173,40 @@ int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void
                     int64_t B, int64_t H, int64_t W, int dtype, const mccb_strides_t *strides,
                     void *workspace, uint64_t workspace_size, void *stream);
 
+/*
+ * Packed variable-length layout (the TND convention of the sibling operators' pages: the tokens of
+ * all sequences packed along one axis, with an INT64 array of cumulative sequence lengths).
+ *
+ *   gradY, x, gradX, y : [T,H] packed tokens, contiguous, 16-byte aligned
+ *   weight, gradWeight : [W,H]
+ *   mask               : optional, one byte per token [T] (nonzero = keep), NULL = all kept
+ *   cu_seqlens         : device int64 [nseq], 8-byte aligned: cu_seqlens[b] is the end of
+ *                        sequence b, which holds tokens cu_seqlens[b-1] .. cu_seqlens[b]-1
+ *                        (cu_seqlens[-1] = 0). Preconditions, not checked (the values live on
+ *                        the device): non-decreasing, last value = T. Violating them gives
+ *                        unspecified outputs but no access outside the buffers.
+ *
+ * Every sequence is its own masked causal conv: the equations of the function description apply
+ * within a sequence, and no stencil reads a token of another sequence (rows past a sequence's end,
+ * or before its start for the forward, are zero); gradWeight sums the terms of all sequences.
+ * This equals the padded [S,B,H] layout with each batch's mask cut at its sequence length.
+ * Limits: T in [1, 524288], nseq in [1, 524288] (empty sequences allowed), H and W as for the
+ * extended calls. Both calls need a workspace (per-token window limits; the backward also holds
+ * its gradWeight partials); sizes from the *_get_workspace_size functions. Same error codes.
+ */
+int mccb_varlen_get_workspace_size(int64_t T, int64_t nseq, int64_t H, int64_t W, int dtype,
+                                   uint64_t *workspace_size);
+int mccb_varlen_backward(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                         const int64_t *cu_seqlens, void *gradX, void *gradWeight, int64_t T,
+                         int64_t nseq, int64_t H, int64_t W, int dtype, void *workspace,
+                         uint64_t workspace_size, void *stream);
+int mccb_varlen_forward_get_workspace_size(int64_t T, int64_t nseq, int64_t H, int64_t W,
+                                           int dtype, uint64_t *workspace_size);
+int mccb_varlen_forward(const void *x, const void *weight, const uint8_t *mask,
+                        const int64_t *cu_seqlens, void *y, int64_t T, int64_t nseq, int64_t H,
+                        int64_t W, int dtype, void *workspace, uint64_t workspace_size,
+                        void *stream);
+
 /* The tiling chosen for a shape, for mccb_backward (first eight fields) and mccb_forward (fwd_*);
  * a pure function of (S, B, H, dtype). Exposed so that tests can place edge cases on tile
  * boundaries. */

@@ -99,6 +99,39 @@ def mccb_forward_ex(x: int, weight: int, mask: int | None, y: int, S: int, B: in
                                      workspace, workspace_size, stream))
 
 
+def mccb_varlen_get_workspace_size(T: int, nseq: int, H: int, W: int, dtype: int) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib().mccb_varlen_get_workspace_size(T, nseq, H, W, dtype, ctypes.byref(out))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_varlen_get_workspace_size")
+    return int(out.value)
+
+
+def mccb_varlen_backward(gradY: int, x: int, weight: int, mask: int | None, cu_seqlens: int,
+                         gradX: int, gradWeight: int, T: int, nseq: int, H: int, W: int,
+                         dtype: int, workspace: int | None, workspace_size: int,
+                         stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_varlen_backward(gradY, x, weight, mask, cu_seqlens, gradX, gradWeight,
+                                          T, nseq, H, W, dtype, workspace, workspace_size, stream))
+
+
+def mccb_varlen_forward_get_workspace_size(T: int, nseq: int, H: int, W: int, dtype: int) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib().mccb_varlen_forward_get_workspace_size(T, nseq, H, W, dtype, ctypes.byref(out))
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_varlen_forward_get_workspace_size")
+    return int(out.value)
+
+
+def mccb_varlen_forward(x: int, weight: int, mask: int | None, cu_seqlens: int, y: int, T: int,
+                        nseq: int, H: int, W: int, dtype: int, workspace: int | None,
+                        workspace_size: int, stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_varlen_forward(x, weight, mask, cu_seqlens, y, T, nseq, H, W, dtype,
+                                         workspace, workspace_size, stream))
+
+
 def mccb_status_string(status: int) -> str:
     return status_string(status)
 
@@ -256,4 +289,79 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
         where = "mccb_forward_ex"
     if rc != MCCB_OK:
         raise MccbError(rc, where)
+    return y
+
+
+def _varlen_args(x, weight, cu_seqlens, mask):
+    if x.dim() != 2:
+        raise ValueError("packed tensors are [T,H]")
+    T, H = (int(v) for v in x.shape)
+    dev, dt = x.device, x.dtype
+    if dt not in DTYPE_CODE:
+        raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
+    _check_tensor("x", x, (T, H), dt, dev)
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a [W,H] tensor")
+    W = int(weight.shape[0])
+    _check_tensor("weight", weight, (W, H), dt, dev)
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor of cumulative sequence ends")
+    _check_tensor("cu_seqlens", cu_seqlens, (int(cu_seqlens.shape[0]),), torch.int64, dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (T,), None, dev)
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be bool or uint8")
+    return T, H, W, int(cu_seqlens.shape[0]), dev, dt
+
+
+def varlen_backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
+                    cu_seqlens: torch.Tensor, mask: torch.Tensor | None = None,
+                    gradX: torch.Tensor | None = None, gradWeight: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None,
+                    stream: torch.cuda.Stream | None = None):
+    """Packed variable-length layout: gradX [T,H], gradWeight [W,H] from gradY, x [T,H], the
+    weight [W,H] and the int64 cumulative sequence ends (device). Enqueues without
+    synchronizing."""
+    T, H, W, nseq, dev, dt = _varlen_args(x, weight, cu_seqlens, mask)
+    _check_tensor("gradY", gradY, (T, H), dt, dev)
+    if gradX is None:
+        gradX = torch.empty((T, H), dtype=dt, device=dev)
+    if gradWeight is None:
+        gradWeight = torch.empty((W, H), dtype=dt, device=dev)
+    _check_tensor("gradX", gradX, (T, H), dt, dev)
+    _check_tensor("gradWeight", gradWeight, (W, H), dt, dev)
+    if workspace is None:
+        n = mccb_varlen_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = mccb_varlen_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
+                              None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
+                              gradX.data_ptr(), gradWeight.data_ptr(), T, nseq, H, W,
+                              DTYPE_CODE[dt], workspace.data_ptr(), workspace.numel(),
+                              st.cuda_stream)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_varlen_backward")
+    return gradX, gradWeight
+
+
+def varlen_forward(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                   mask: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None,
+                   stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Packed variable-length layout: y [T,H] = mask * causal depthwise conv(x, weight) within
+    each sequence. Enqueues without synchronizing."""
+    T, H, W, nseq, dev, dt = _varlen_args(x, weight, cu_seqlens, mask)
+    if y is None:
+        y = torch.empty((T, H), dtype=dt, device=dev)
+    _check_tensor("y", y, (T, H), dt, dev)
+    if workspace is None:
+        n = mccb_varlen_forward_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = mccb_varlen_forward(x.data_ptr(), weight.data_ptr(),
+                             None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
+                             y.data_ptr(), T, nseq, H, W, DTYPE_CODE[dt], workspace.data_ptr(),
+                             workspace.numel(), st.cuda_stream)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_varlen_forward")
     return y

@@ -61,6 +61,18 @@ def lib() -> ctypes.CDLL:
         L.mccb_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, sp, vp, u64,
                                       vp]
         L.mccb_forward_ex.restype = ctypes.c_int
+        L.mccb_varlen_get_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int,
+                                                     ctypes.POINTER(u64)]
+        L.mccb_varlen_get_workspace_size.restype = ctypes.c_int
+        L.mccb_varlen_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                           ctypes.c_int, vp, u64, vp]
+        L.mccb_varlen_backward.restype = ctypes.c_int
+        L.mccb_varlen_forward_get_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int,
+                                                             ctypes.POINTER(u64)]
+        L.mccb_varlen_forward_get_workspace_size.restype = ctypes.c_int
+        L.mccb_varlen_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, vp,
+                                          u64, vp]
+        L.mccb_varlen_forward.restype = ctypes.c_int
         L.mccb_status_string.argtypes = [ctypes.c_int]
         L.mccb_status_string.restype = ctypes.c_char_p
         L.mccb_profile_begin.argtypes = [ctypes.c_int]

@@ -195,10 +195,12 @@ __device__ static inline void store_vec(vec_t *p, vec_t v) {
 
 // gradX for one lane's kVec columns at row i from the masked gradY rows i .. i+W-1 (fp64, d[k] =
 // gYm[i+k]), and the gradWeight terms of row i: a[k] += gYm[i+W-1-k] * x[i]. Returns the packed
-// gradX row.
-template <int DT, int W>
+// gradX row. LIMITED (packed variable-length layout): only d[k] with k < lim belong to row i's
+// sequence; the rest count as zero.
+template <int DT, int W, bool LIMITED = false>
 __device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec_t x_row,
-                                           const double (&wt)[W][kVec], double (&a)[W][kVec]) {
+                                           const double (&wt)[W][kVec], double (&a)[W][kVec],
+                                           int lim = W) {
     float xf[kVec];
     unpack_vec<DT>(x_row, xf);
     float out[kVec];
@@ -207,7 +209,8 @@ __device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec
         // gradX[i] = sum_k gYm[i+k] * w[W-1-k], in k order (each product exact in fp64)
         double s = d[0][e] * wt[W - 1][e];
 #pragma unroll
-        for (int k = 1; k < W; ++k) s = __builtin_fma(d[k][e], wt[W - 1 - k][e], s);
+        for (int k = 1; k < W; ++k)
+            s = __builtin_fma((!LIMITED || k < lim) ? d[k][e] : 0.0, wt[W - 1 - k][e], s);
 #if MCCB_EXACT_GRADX
         out[e] = round_to_odd_f32(s);
 #else
@@ -216,7 +219,9 @@ __device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec
         // gradWeight[k] += gYm[i+W-1-k] * x[i]
         const double xd = (double)xf[e];
 #pragma unroll
-        for (int k = 0; k < W; ++k) a[k][e] = __builtin_fma(d[W - 1 - k][e], xd, a[k][e]);
+        for (int k = 0; k < W; ++k)
+            a[k][e] = __builtin_fma((!LIMITED || W - 1 - k < lim) ? d[W - 1 - k][e] : 0.0, xd,
+                                    a[k][e]);
     }
     vec_t r;
 #pragma unroll
@@ -257,13 +262,17 @@ constexpr int fused_waves_per_simd(bool strided, int w) {
     return (strided || w > 3) ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD;
 }
 
-template <int DT, bool HAS_MASK, bool STRIDED, int W>
+// VARLEN (packed variable-length layout, B = 1): `ahead[i]` holds the number of rows i, i+1, ...
+// that belong to row i's sequence (at least 1); the stencil of row i uses only those. The bytes of
+// the strip are staged in LDS after the mask's `lim_lds` bytes.
+template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
 __global__ void __launch_bounds__(kBlockWaves *kWave)
     __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(STRIDED, W))))
     mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
                    const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
                    vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
-                   int64_t rows_per_strip, int64_t n_col_blocks, InStrides st) {
+                   int64_t rows_per_strip, int64_t n_col_blocks, InStrides st,
+                   const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
     constexpr int L = W - 1;  // look-ahead rows
     extern __shared__ uint8_t smask[];
     __shared__ f64x2 red[kBlockWaves][kWave * kVec / 2];
@@ -302,8 +311,21 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
             smask[t] = (row < S) ? mask[(j_first + jj) * st.m_batch + row * st.m_row] : (uint8_t)0;
         }
         moff = (int)(j - j_first) * span;
+        if constexpr (!VARLEN) __syncthreads();
+    }
+    if constexpr (VARLEN) {
+        const int span = (int)(rows_per_strip + L);
+        for (int t = threadIdx.x; t < span; t += blockDim.x) {
+            const int64_t row = rs0 + t;
+            smask[lim_lds + t] = (row < S) ? ahead[row] : (uint8_t)1;
+        }
         __syncthreads();
     }
+    // rows of the output row's sequence from that row on (VARLEN), the same for every lane
+    auto lim_of = [&](int64_t row) -> int {
+        if constexpr (VARLEN) return __builtin_amdgcn_readfirstlane(smask[lim_lds + (int)(row - rs0)]);
+        return W;
+    };
 
     double wt[W][kVec];
 #pragma unroll
@@ -378,7 +400,17 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 #pragma unroll
         for (int u = 0; u < kTurnRows; ++u) {
             widen<DT>(keep(i0 + L + u) ? qy[u + L] : zero, d[L]);
-            const vec_t r = stencil_row<DT, W>(d, qx[u], wt, a);
+            vec_t r;
+            if constexpr (VARLEN) {
+                // a uniform branch: only the last W-1 rows of a sequence take the limited form
+                const int lim = lim_of(i0 + u);
+                if (lim >= W)
+                    r = stencil_row<DT, W>(d, qx[u], wt, a);
+                else
+                    r = stencil_row<DT, W, true>(d, qx[u], wt, a, lim);
+            } else {
+                r = stencil_row<DT, W>(d, qx[u], wt, a);
+            }
             if (active) store_vec(out_at(i0 + u), r);
 #pragma unroll
             for (int k = 0; k < L; ++k)
@@ -398,7 +430,8 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
             widen<DT>((i0 + k < S && keep(i0 + k)) ? load_vec_cached(at_gy(i0 + k)) : zero, d[k]);
         for (int64_t i = i0; i < i1; ++i) {
             widen<DT>((i + L < S && keep(i + L)) ? load_vec_cached(at_gy(i + L)) : zero, d[L]);
-            const vec_t r = stencil_row<DT, W>(d, load_vec(at_x(i)), wt, a);
+            const vec_t r = VARLEN ? stencil_row<DT, W, true>(d, load_vec(at_x(i)), wt, a, lim_of(i))
+                                   : stencil_row<DT, W>(d, load_vec(at_x(i)), wt, a);
             if (active) store_vec(out_at(i), r);
 #pragma unroll
             for (int k = 0; k < L; ++k)
@@ -504,9 +537,9 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
 // rows before 0 read as 0 (the causal depthwise conv the backward above differentiates; W = 3 on
 // the page). Pure streaming: read x, write y, nothing to reduce.
 //
-// A block covers a short tile: kFwdRows rows x kFwdCols contiguous columns (kFwdWaves wavefronts
-// side by side, kFwdVec channels per lane; 8 rows x 4096 columns by default). Tiles are numbered
-// row-major, column tile fastest, so the blocks in flight at any moment sit on a few neighbouring
+// A block covers a short tile of contiguous columns (kFwdWaves wavefronts, kFwdVec channels per
+// lane; 8 rows x 4096 columns when B*H is large, see `cw` below). Tiles are numbered row-major,
+// column tile fastest, so the blocks in flight at any moment sit on a few neighbouring
 // rows; the HBM serves such a compact front markedly faster than many independent column walks.
 // The W-1 rows before the tile are re-read with cached loads (the tile above loaded them, also
 // cached, as its last rows); when the column-tile count is a multiple of the 8 XCDs, which take
@@ -519,10 +552,10 @@ constexpr int kFwdVec = MCCB_FWD_VEC;
 constexpr int kFwdWords = kFwdVec / 2;
 constexpr int kFwdWaves = MCCB_FWD_WAVES;
 constexpr int kFwdRows = MCCB_FWD_ROWS;
-constexpr int kFwdCols = kFwdWaves * kWave * kFwdVec;  // columns of one tile
 static_assert(kFwdVec == 2 || kFwdVec == 4 || kFwdVec == 8, "forward lane vector: 4, 8 or 16 bytes");
 static_assert(kFwdRows >= 3, "the look-back rows (up to 3) come from the tile above");
 static_assert(kFwdWaves * kWave <= 1024, "forward block too large");
+static_assert((kFwdWaves & (kFwdWaves - 1)) == 0, "forward waves per block: a power of two");
 
 typedef uint32_t fvec_t __attribute__((ext_vector_type(kFwdWords)));
 
@@ -537,11 +570,19 @@ __device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
     }
 }
 
-template <int DT, bool HAS_MASK, bool STRIDED, int W>
+// VARLEN (packed variable-length layout, B = 1): `behind[i]` holds the number of rows before row i
+// that belong to its sequence; the window of row i uses only those.
+//
+// `cw` (1, 2, 4 or kFwdWaves, chosen by the host) is how many of the block's waves sit side by side
+// across the columns; the rest stack along the rows, so a block covers (kFwdWaves / cw) * kFwdRows
+// rows x cw * kWave * kFwdVec columns. Narrow rows (the packed layout's H columns, or a small
+// B*H) use fewer columns per block instead of leaving lanes idle.
+template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
-             int64_t H, int64_t n_ct, InStrides st) {
+             int64_t H, int64_t n_ct, int cw, InStrides st,
+             const uint8_t *__restrict__ behind = nullptr) {
     constexpr int L = W - 1;  // look-back rows
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
     if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
@@ -549,14 +590,16 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     const int64_t rt = blockIdx.x / n_ct;  // row tile
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wc = wave % cw, wr = wave / cw;  // the wave's column slot and row slot
     const int64_t C = B * H;
-    const int64_t c0 = ct * kFwdCols + (int64_t)wave * (kWave * kFwdVec) + lane * kFwdVec;
+    const int64_t c0 = (ct * cw + wc) * (int64_t)(kWave * kFwdVec) + lane * kFwdVec;
     if (c0 >= C) return;  // no barrier below: lanes past the last column just leave
     const int64_t CV = C / kFwdVec;  // lane vectors per row (C is a multiple of 64)
     const int64_t v = c0 / kFwdVec;
     const int64_t h0 = c0 % H;  // the lane's kFwdVec channels share one batch: H % 64 == 0
     const int64_t j = c0 / H;
-    const int64_t r0 = rt * kFwdRows;
+    const int64_t r0 = (rt * (kFwdWaves / cw) + wr) * kFwdRows;
+    if (r0 >= S) return;
 
     // x rows r0-L .. r0+kFwdRows-1; rows outside [0, S) are zero
     fvec_t xr[kFwdRows + L];
@@ -579,6 +622,16 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     uint8_t keep[kFwdRows];
 #pragma unroll
     for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
+    int first[kFwdRows];  // first window position inside the row's sequence
+#pragma unroll
+    for (int u = 0; u < kFwdRows; ++u) first[u] = 0;
+    if constexpr (VARLEN) {
+#pragma unroll
+        for (int u = 0; u < kFwdRows; ++u) {
+            const int b = (r0 + u < S) ? (int)behind[r0 + u] : L;
+            first[u] = L - (b < L ? b : L);
+        }
+    }
     if (HAS_MASK) {
         const uint8_t *mrow = mask + j * st.m_batch + r0 * st.m_row;
 #pragma unroll
@@ -596,9 +649,10 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
 #pragma unroll
         for (int e = 0; e < kFwdVec; ++e) {
             // y[i] = sum_k w[k] x[i-L+k], in k order, exact in fp64, rounded once
-            double s = win[0][e] * wt[0][e];
+            double s = ((!VARLEN || 0 >= first[u]) ? win[0][e] : 0.0) * wt[0][e];
 #pragma unroll
-            for (int k = 1; k < W; ++k) s = __builtin_fma(win[k][e], wt[k][e], s);
+            for (int k = 1; k < W; ++k)
+                s = __builtin_fma((!VARLEN || k >= first[u]) ? win[k][e] : 0.0, wt[k][e], s);
             out[e] = keep[u] ? round_to_odd_f32(s) : 0.0f;
         }
         fvec_t r;
@@ -629,6 +683,35 @@ __global__ void __launch_bounds__(256)
         const uint32_t lo = row[(2 * q) * s2], hi = row[(2 * q + 1) * s2];
         out[q] = lo | (hi << 16);
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Packed variable-length layout: per-token window limits from the cumulative sequence ends cu[]
+// (sequence b holds tokens cu[b-1] .. cu[b]-1, cu[-1] = 0). One thread per token, a binary search
+// for the first end past it. ahead[t] = tokens t.. up to its sequence's end (1..255, clamped);
+// behind[t] = tokens of its sequence before t (0..255, clamped). A malformed cu (decreasing, or
+// not ending at T) gives clamped limits, never an access outside [0, T).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+    mccb_seg_limits(const int64_t *__restrict__ cu, int64_t nseq, int64_t T,
+                    uint8_t *__restrict__ ahead, uint8_t *__restrict__ behind) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    int64_t lo = 0, hi = nseq;  // first b with cu[b] > t, or nseq
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (cu[mid] > t) hi = mid;
+        else lo = mid + 1;
+    }
+    int64_t start = lo == 0 ? 0 : cu[lo - 1];
+    int64_t end = lo < nseq ? cu[lo] : T;
+    if (start > t) start = t;
+    if (start < 0) start = 0;
+    if (end <= t) end = t + 1;
+    if (end > T) end = T;
+    const int64_t a = end - t, b = t - start;
+    ahead[t] = (uint8_t)(a > 255 ? 255 : a);
+    if (behind) behind[t] = (uint8_t)(b > 255 ? 255 : b);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -744,15 +827,30 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     return e;
 }
 
-// Forward grid: column tiles times row tiles, column tile fastest.
+// Forward grid: column tiles times row tiles, column tile fastest. The block's waves sit
+// side by side across as many columns as the row can fill without idling more than 1/8 of its
+// lanes (all kFwdWaves when B*H is large), and stack along the rows otherwise.
 struct FwdPlan {
-    int64_t n_ct, n_rt;
+    int64_t n_ct, n_rt, rows, cols;
+    int cw;
 };
 
 FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
+    const int64_t C = B * H, wave_cols = kWave * kFwdVec;
     FwdPlan f;
-    f.n_ct = (B * H + kFwdCols - 1) / kFwdCols;
-    f.n_rt = (S + kFwdRows - 1) / kFwdRows;
+    f.cw = 1;
+    for (int cw = kFwdWaves; cw >= 1; cw /= 2) {
+        const int64_t span = cw * wave_cols;
+        const int64_t waste = (C + span - 1) / span * span - C;
+        if (waste * 8 <= C) {
+            f.cw = cw;
+            break;
+        }
+    }
+    f.cols = f.cw * wave_cols;
+    f.rows = (int64_t)(kFwdWaves / f.cw) * kFwdRows;
+    f.n_ct = (C + f.cols - 1) / f.cols;
+    f.n_rt = (S + f.rows - 1) / f.rows;
     return f;
 }
 
@@ -765,7 +863,8 @@ hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, int W, const void *x, con
     const dim3 block(kFwdWaves * kWave);
 #define MCCB_FWD(M, T, TAPS)                                                                      \
     hipLaunchKernelGGL((mccb_fwd<DT, M, T, TAPS>), grid, block, MCCB_FWD_LDS, st,                \
-                       (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct, is)
+                       (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct,  \
+                       f.cw, is)
 #define MCCB_FWD_W(TAPS)                                                                          \
     if (mask) {                                                                                   \
         if (strided) MCCB_FWD(true, true, TAPS); else MCCB_FWD(true, false, TAPS);                \
@@ -904,6 +1003,107 @@ bool any_overlap(const void *const *bufs, const uint64_t *lens, int n, int first
     return false;
 }
 
+// Packed variable-length layout: the backward and forward run with B = 1, S = T, after the
+// per-token limits are computed into the workspace.
+template <int DT>
+hipError_t launch_varlen_bwd(const Plan &p, const void *gy, const void *x, const void *w,
+                             const uint8_t *mask, const int64_t *cu, int64_t nseq, void *gx,
+                             void *gw, void *ws, uint64_t lim_off, hipStream_t st) {
+    uint8_t *ahead = (uint8_t *)ws + lim_off;
+    const int64_t T = p.S;
+    hipLaunchKernelGGL(mccb_seg_limits, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, cu,
+                       nseq, T, ahead, (uint8_t *)nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
+    const dim3 block1(kBlockWaves * kWave);
+    const int span = (int)(p.rows_per_strip + p.W - 1);
+    const int lim_lds = mask ? (int)p.mask_lds : 0;
+    const size_t lds = (size_t)lim_lds + (size_t)span;
+    const InStrides is{p.H, p.H, p.H, p.H, T, 1};
+#define MCCB_VL(M, TAPS)                                                                          \
+    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, false, TAPS, true>), grid1, block1, lds, st,       \
+                       (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx,  \
+                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, p.n_col_blocks, is, ahead,  \
+                       lim_lds)
+#define MCCB_VL_W(TAPS)                                                                           \
+    if (mask) MCCB_VL(true, TAPS); else MCCB_VL(false, TAPS);
+    switch (p.W) {
+        case 1: MCCB_VL_W(1); break;
+        case 2: MCCB_VL_W(2); break;
+        case 3: MCCB_VL_W(3); break;
+        case 4: MCCB_VL_W(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MCCB_VL_W
+#undef MCCB_VL
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
+    const dim3 block2(kReduceWaves * kWave);
+    hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
+                       (uint32_t *)gw, p.n_strips, p.B, p.H);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_varlen_fwd(int64_t T, int64_t H, int W, const void *x, const void *w,
+                             const uint8_t *mask, const int64_t *cu, int64_t nseq, void *y,
+                             void *ws, uint64_t behind_off, hipStream_t st) {
+    uint8_t *ahead = (uint8_t *)ws, *behind = (uint8_t *)ws + behind_off;
+    hipLaunchKernelGGL(mccb_seg_limits, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, cu,
+                       nseq, T, ahead, behind);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const FwdPlan f = make_fwd_plan(T, 1, H);
+    const dim3 grid((unsigned)(f.n_ct * f.n_rt));
+    const dim3 block(kFwdWaves * kWave);
+    const InStrides is{H, H, H, H, T, 1};
+#define MCCB_VLF(M, TAPS)                                                                         \
+    hipLaunchKernelGGL((mccb_fwd<DT, M, false, TAPS, true>), grid, block, MCCB_FWD_LDS, st,      \
+                       (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, T, (int64_t)1, H, \
+                       f.n_ct, f.cw, is, behind)
+#define MCCB_VLF_W(TAPS)                                                                          \
+    if (mask) MCCB_VLF(true, TAPS); else MCCB_VLF(false, TAPS);
+    switch (W) {
+        case 1: MCCB_VLF_W(1); break;
+        case 2: MCCB_VLF_W(2); break;
+        case 3: MCCB_VLF_W(3); break;
+        case 4: MCCB_VLF_W(4); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MCCB_VLF_W
+#undef MCCB_VLF
+    return hipGetLastError();
+}
+
+// Workspace of the packed layout: [fp64 partials][per-token limits], or for the forward
+// [ahead][behind]; each part 256-byte aligned.
+struct VarlenLayout {
+    uint64_t lim_off, total;
+};
+
+VarlenLayout varlen_bwd_layout(const Plan &p) {
+    VarlenLayout v;
+    v.lim_off = align256(p.ws_bytes);
+    v.total = v.lim_off + (uint64_t)p.S;
+    return v;
+}
+
+VarlenLayout varlen_fwd_layout(int64_t T) {
+    VarlenLayout v;
+    v.lim_off = align256((uint64_t)T);  // behind[]
+    v.total = v.lim_off + (uint64_t)T;
+    return v;
+}
+
+int check_varlen(int64_t T, int64_t nseq, int64_t H, int64_t W, int dtype) {
+    int rc = check_shape(T, 1, H, dtype);  // T tokens in [1, 524288], H as usual
+    if (rc == MCCB_OK) rc = check_taps(W);
+    if (rc == MCCB_OK && (nseq < 1 || nseq > kMaxBS)) rc = MCCB_ERR_SHAPE;
+    return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -930,8 +1130,8 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     plan->waves_per_block = kBlockWaves;
     plan->workspace_size = p.ws_bytes;
     const FwdPlan f = make_fwd_plan(S, B, H);
-    plan->fwd_rows_per_tile = kFwdRows;
-    plan->fwd_cols_per_tile = kFwdCols;
+    plan->fwd_rows_per_tile = f.rows;
+    plan->fwd_cols_per_tile = f.cols;
     plan->fwd_n_col_tiles = f.n_ct;
     plan->fwd_n_row_tiles = f.n_rt;
     return MCCB_OK;
@@ -1124,6 +1324,80 @@ int mccb_forward_ex(const void *x, const void *weight, const uint8_t *mask, void
         (dtype == MCCB_BF16)
             ? launch_fwd<MCCB_BF16>(S, B, H, (int)W, x_eff, w_eff, mask, y, st, is, strided)
             : launch_fwd<MCCB_FP16>(S, B, H, (int)W, x_eff, w_eff, mask, y, st, is, strided);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+int mccb_varlen_get_workspace_size(int64_t T, int64_t nseq, int64_t H, int64_t W, int dtype,
+                                   uint64_t *workspace_size) {
+    if (!workspace_size) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_varlen(T, nseq, H, W, dtype);
+    if (rc != MCCB_OK) return rc;
+    *workspace_size = varlen_bwd_layout(make_plan(T, 1, H, dtype, (int)W)).total;
+    return MCCB_OK;
+}
+
+int mccb_varlen_backward(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
+                         const int64_t *cu_seqlens, void *gradX, void *gradWeight, int64_t T,
+                         int64_t nseq, int64_t H, int64_t W, int dtype, void *workspace,
+                         uint64_t workspace_size, void *stream) {
+    if (!gradY || !x || !weight || !cu_seqlens || !gradX || !gradWeight)
+        return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_varlen(T, nseq, H, W, dtype);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(T, 1, H, dtype, (int)W);
+    const VarlenLayout L = varlen_bwd_layout(p);
+    if (!workspace) return MCCB_ERR_PARAM_NULLPTR;
+    if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
+    if (!aligned16(gradY) || !aligned16(x) || !aligned16(weight) || !aligned16(gradX) ||
+        !aligned16(gradWeight) || !aligned16(workspace) || ((uintptr_t)cu_seqlens & 7u))
+        return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(T * H) * 2u, wb = (uint64_t)(W * H) * 2u;
+    const void *bufs[8] = {gradY, x, weight, mask, cu_seqlens, gradX, gradWeight, workspace};
+    const uint64_t lens[8] = {nb, nb, wb, mask ? (uint64_t)T : 0u, (uint64_t)nseq * 8u,
+                              nb, wb, L.total};
+    if (any_overlap(bufs, lens, 8, 5)) return MCCB_ERR_PARAM_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e =
+        (dtype == MCCB_BF16)
+            ? launch_varlen_bwd<MCCB_BF16>(p, gradY, x, weight, mask, cu_seqlens, nseq, gradX,
+                                           gradWeight, workspace, L.lim_off, st)
+            : launch_varlen_bwd<MCCB_FP16>(p, gradY, x, weight, mask, cu_seqlens, nseq, gradX,
+                                           gradWeight, workspace, L.lim_off, st);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+int mccb_varlen_forward_get_workspace_size(int64_t T, int64_t nseq, int64_t H, int64_t W,
+                                           int dtype, uint64_t *workspace_size) {
+    if (!workspace_size) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_varlen(T, nseq, H, W, dtype);
+    if (rc != MCCB_OK) return rc;
+    *workspace_size = varlen_fwd_layout(T).total;
+    return MCCB_OK;
+}
+
+int mccb_varlen_forward(const void *x, const void *weight, const uint8_t *mask,
+                        const int64_t *cu_seqlens, void *y, int64_t T, int64_t nseq, int64_t H,
+                        int64_t W, int dtype, void *workspace, uint64_t workspace_size,
+                        void *stream) {
+    if (!x || !weight || !cu_seqlens || !y) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_varlen(T, nseq, H, W, dtype);
+    if (rc != MCCB_OK) return rc;
+    const VarlenLayout L = varlen_fwd_layout(T);
+    if (!workspace) return MCCB_ERR_PARAM_NULLPTR;
+    if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(y) || ((uintptr_t)cu_seqlens & 7u))
+        return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(T * H) * 2u, wb = (uint64_t)(W * H) * 2u;
+    const void *bufs[6] = {x, weight, mask, cu_seqlens, y, workspace};
+    const uint64_t lens[6] = {nb, wb, mask ? (uint64_t)T : 0u, (uint64_t)nseq * 8u, nb, L.total};
+    if (any_overlap(bufs, lens, 6, 4)) return MCCB_ERR_PARAM_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e =
+        (dtype == MCCB_BF16)
+            ? launch_varlen_fwd<MCCB_BF16>(T, H, (int)W, x, weight, mask, cu_seqlens, nseq, y,
+                                           workspace, L.lim_off, st)
+            : launch_varlen_fwd<MCCB_FP16>(T, H, (int)W, x, weight, mask, cu_seqlens, nseq, y,
+                                           workspace, L.lim_off, st);
     return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
 }
 

@@ -60,6 +60,13 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_backward_w.restype = ctypes.c_int
     lib.oracle_forward_w.argtypes = [ctypes.c_int, i64, i64, i64, _f64p, _f64p, _u8p, _f64p]
     lib.oracle_forward_w.restype = ctypes.c_int
+    _i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_backward_varlen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, _i64p, _u16p,
+                                           _u16p, _u16p, _u8p, _f64p, _u16p, _f64p, _f64p, _u16p]
+    lib.oracle_backward_varlen.restype = ctypes.c_int
+    lib.oracle_forward_varlen.argtypes = [ctypes.c_int, i64, i64, i64, _i64p, _f64p, _f64p, _u8p,
+                                          _f64p]
+    lib.oracle_forward_varlen.restype = ctypes.c_int
     return lib
 
 
@@ -159,6 +166,57 @@ class Oracle:
         x64 = self.decode(dtype, np.ascontiguousarray(x16, dtype=np.uint16))
         w64 = self.decode(dtype, np.ascontiguousarray(w16, dtype=np.uint16))
         y64 = self.forward(x64, w64, mask)
+        return {"y64": y64, "y16": self.encode(dtype, y64)}
+
+
+    # -- packed variable-length layout ------------------------------------------------------------
+    def backward_varlen(self, dtype: str, gY: np.ndarray, x: np.ndarray, w: np.ndarray,
+                        cu: np.ndarray, mask: np.ndarray | None, want_gx64: bool = True) -> dict:
+        """gY, x: uint16 [T,H] packed tokens; w: uint16 [W,H]; cu: int64 [n] cumulative sequence
+        ends (cu[-1] == T); mask: uint8/bool [T] or None. Same outputs as backward()."""
+        gY = np.ascontiguousarray(gY, dtype=np.uint16)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        cu = np.ascontiguousarray(cu, dtype=np.int64)
+        T, H = gY.shape
+        W = int(w.shape[0])
+        if x.shape != (T, H) or w.shape != (W, H):
+            raise ValueError("gY, x must be [T,H] and w [W,H]")
+        m = None if mask is None else np.ascontiguousarray(mask).astype(np.uint8, copy=False)
+        out = {"gx16": np.empty((T, H), np.uint16), "gw16": np.empty((W, H), np.uint16),
+               "gw64": np.empty((W, H), np.float64), "gwrss": np.empty((W, H), np.float64)}
+        if want_gx64:
+            out["gx64"] = np.empty((T, H), np.float64)
+        rc = self.lib.oracle_backward_varlen(
+            DTYPE_CODE[dtype], W, T, H, cu.size, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            _ptr(gY, _u16p), _ptr(x, _u16p), _ptr(w, _u16p), None if m is None else _ptr(m, _u8p),
+            _ptr(out["gx64"], _f64p) if want_gx64 else None, _ptr(out["gx16"], _u16p),
+            _ptr(out["gw64"], _f64p), _ptr(out["gwrss"], _f64p), _ptr(out["gw16"], _u16p))
+        if rc != 0:
+            raise RuntimeError(f"oracle_backward_varlen failed ({rc})")
+        return out
+
+    def forward_varlen(self, x64: np.ndarray, w64: np.ndarray, cu: np.ndarray,
+                       mask: np.ndarray | None) -> np.ndarray:
+        x64 = np.ascontiguousarray(x64, dtype=np.float64)
+        w64 = np.ascontiguousarray(w64, dtype=np.float64)
+        cu = np.ascontiguousarray(cu, dtype=np.int64)
+        T, H = x64.shape
+        m = None if mask is None else np.ascontiguousarray(mask).astype(np.uint8, copy=False)
+        y = np.empty_like(x64)
+        rc = self.lib.oracle_forward_varlen(
+            int(w64.shape[0]), T, H, cu.size, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            _ptr(x64, _f64p), _ptr(w64, _f64p), None if m is None else _ptr(m, _u8p),
+            _ptr(y, _f64p))
+        if rc != 0:
+            raise RuntimeError(f"oracle_forward_varlen failed ({rc})")
+        return y
+
+    def forward16_varlen(self, dtype: str, x16: np.ndarray, w16: np.ndarray, cu: np.ndarray,
+                         mask: np.ndarray | None) -> dict:
+        x64 = self.decode(dtype, np.ascontiguousarray(x16, dtype=np.uint16))
+        w64 = self.decode(dtype, np.ascontiguousarray(w16, dtype=np.uint16))
+        y64 = self.forward_varlen(x64, w64, cu, mask)
         return {"y64": y64, "y16": self.encode(dtype, y64)}
 
 

@@ -248,3 +248,105 @@ int oracle_forward(int64_t S, int64_t B, int64_t H, const double *x, const doubl
                    const uint8_t *mask, double *y) {
     return oracle_forward_w(OR_TAPS, S, B, H, x, w, mask, y);
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Packed variable-length layout. The sibling operators' pages describe a TND layout: the tokens of
+ * all sequences packed along one axis T, with an INT64 array of per-sequence lengths given as
+ * cumulative sums (the actualSeqLengths parameter). Here gY, x, gX and y are [T,H], the mask, if
+ * any, is one byte per token [T], and cu[b] is the end of sequence b: sequence b holds the tokens
+ * cu[b-1] .. cu[b]-1 (cu[-1] = 0), and cu[nseq-1] must equal T. Each sequence is its own
+ * [S = length, B = 1] problem: the stencil never reads across a sequence boundary (rows past the
+ * end of a sequence, or before its start for the forward, are zero), and gradWeight sums the terms
+ * of every sequence.
+ * --------------------------------------------------------------------------------------------- */
+
+static int check_cu(int64_t T, int64_t nseq, const int64_t *cu) {
+    if (nseq < 1 || !cu) return -1;
+    int64_t prev = 0;
+    for (int64_t b = 0; b < nseq; ++b) {
+        if (cu[b] < prev) return -1;
+        prev = cu[b];
+    }
+    return prev == T ? 0 : -1;
+}
+
+int oracle_backward_varlen(int dtype, int W, int64_t T, int64_t H, int64_t nseq, const int64_t *cu,
+                           const uint16_t *gY, const uint16_t *x, const uint16_t *w,
+                           const uint8_t *mask, double *gx64, uint16_t *gx16, double *gw64,
+                           double *gwrss, uint16_t *gw16) {
+    if (T < 1 || H < 1 || W < 1 || W > 8 || !gY || !x || !w) return -1;
+    if (dtype != OR_BF16 && dtype != OR_FP16) return -1;
+    if (check_cu(T, nseq, cu) != 0) return -1;
+    double *gyd = (double *)malloc(sizeof(double) * (size_t)(T * H));
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(T * H));
+    double *wd = (double *)malloc(sizeof(double) * (size_t)(W * H));
+    if (!gyd || !xd || !wd) {
+        free(gyd);
+        free(xd);
+        free(wd);
+        return -1;
+    }
+    oracle_decode(dtype, gY, gyd, T * H);
+    oracle_decode(dtype, x, xd, T * H);
+    oracle_decode(dtype, w, wd, (int64_t)W * H);
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < H; ++h) {
+        double acc_w[8] = {0}, sq_w[8] = {0}; /* W <= 8 (checked above) */
+        for (int64_t b = 0; b < nseq; ++b) {
+            const int64_t start = b == 0 ? 0 : cu[b - 1], end = cu[b];
+            for (int64_t t = start; t < end; ++t) {
+                /* gradX[t] = sum_k gYm[t+k] * w[W-1-k], rows past the sequence end are zero */
+                double acc = 0.0;
+                for (int k = 0; k < W; ++k) {
+                    const int64_t r = t + k;
+                    if (r >= end) break;
+                    const double m = (mask == NULL || mask[r] != 0) ? 1.0 : 0.0;
+                    acc += m * gyd[r * H + h] * wd[(W - 1 - k) * H + h];
+                }
+                if (gx64) gx64[t * H + h] = acc;
+                if (gx16) gx16[t * H + h] = encode_one(dtype, acc);
+                /* gradWeight[k] += gYm[t+W-1-k] * x[t], within the sequence */
+                for (int k = 0; k < W; ++k) {
+                    const int64_t r = t + W - 1 - k;
+                    if (r >= end) continue;
+                    const double m = (mask == NULL || mask[r] != 0) ? 1.0 : 0.0;
+                    const double term = m * gyd[r * H + h] * xd[t * H + h];
+                    acc_w[k] += term;
+                    sq_w[k] += term * term;
+                }
+            }
+        }
+        for (int k = 0; k < W; ++k) {
+            if (gw64) gw64[k * H + h] = acc_w[k];
+            if (gwrss) gwrss[k * H + h] = sqrt(sq_w[k]);
+            if (gw16) gw16[k * H + h] = encode_one(dtype, acc_w[k]);
+        }
+    }
+    free(gyd);
+    free(xd);
+    free(wd);
+    return 0;
+}
+
+int oracle_forward_varlen(int W, int64_t T, int64_t H, int64_t nseq, const int64_t *cu,
+                          const double *x, const double *w, const uint8_t *mask, double *y) {
+    if (T < 1 || H < 1 || W < 1 || !x || !w || !y) return -1;
+    if (check_cu(T, nseq, cu) != 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t b = 0; b < nseq; ++b) {
+            const int64_t start = b == 0 ? 0 : cu[b - 1], end = cu[b];
+            for (int64_t t = start; t < end; ++t) {
+                double acc = 0.0;
+                for (int k = 0; k < W; ++k) {
+                    const int64_t src = t - (W - 1) + k;
+                    if (src < start) continue; /* nothing before the sequence's first token */
+                    acc += w[k * H + h] * x[src * H + h];
+                }
+                const double m = (mask == NULL || mask[t] != 0) ? 1.0 : 0.0;
+                y[t * H + h] = m * acc;
+            }
+        }
+    }
+    return 0;
+}

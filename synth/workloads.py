@@ -159,3 +159,31 @@ def host_inputs(wl: Workload) -> dict:
 def bits(t: torch.Tensor):
     """numpy uint16 view of a bf16/fp16 tensor's bit patterns (on the CPU)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
+
+
+# -- packed variable-length layout ---------------------------------------------------------------------
+def varlen_lengths(wl: Workload) -> torch.Tensor:
+    """Sequence lengths of the packed form of a workload: its batches' valid-prefix lengths
+    (uniform integers in [S/2, S], as for the prefix mask)."""
+    return prefix_lengths(wl)
+
+
+def pack_index(lengths) -> tuple:
+    """(row, batch) index tensors that gather a padded [S,B,...] tensor's valid tokens into the
+    packed [T,...] order (batch-major: sequence 0's tokens first)."""
+    lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    batch = torch.repeat_interleave(torch.arange(lengths.numel(), dtype=torch.int64), lengths)
+    starts = torch.cumsum(lengths, 0) - lengths
+    row = torch.arange(int(lengths.sum()), dtype=torch.int64) - torch.repeat_interleave(starts, lengths)
+    return row, batch
+
+
+def pack_tokens(t: torch.Tensor, lengths) -> torch.Tensor:
+    """Packed [T,H] copy of the valid tokens of a padded [S,B,H] tensor (same device)."""
+    row, batch = pack_index(lengths)
+    return t[row.to(t.device), batch.to(t.device)].contiguous()
+
+
+def cu_seqlens(lengths, device="cpu") -> torch.Tensor:
+    """Cumulative sequence ends (int64), the packed layout's sequence description."""
+    return torch.cumsum(torch.as_tensor(lengths, dtype=torch.int64), 0).to(device)

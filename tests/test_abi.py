@@ -328,3 +328,46 @@ def test_ex_weight_extent_follows_taps():
     H = 384
     assert xcall(taps=4, gw=W + 3 * H * 2 + 256 - (3 * H * 2) % 256) == INVALID
     assert xcall(taps=4, gx=W + 3 * H * 2) == INVALID
+
+
+# -- packed variable-length layout (mccb_varlen_*) --------------------------------------------------
+CU = 0x7F0000000000 + 7 * 64 * GB
+
+
+def vcall(gy=GY, x=X, w=W, m=M, cu=CU, gx=GX, gw=GW, T=100, nseq=3, H=384, taps=3, dt=BF16, ws=WS,
+          wsz=1 << 40):
+    rc = mdc.mccb_varlen_backward(gy, x, w, m, cu, gx, gw, T, nseq, H, taps, dt, ws, wsz, None)
+    assert rc in VALIDATION_CODES, f"varlen call passed validation with fake pointers (rc={rc})"
+    return rc
+
+
+def test_varlen_workspace_sizes():
+    T, H = 1000, 384
+    p = mdc.mccb_get_plan(T, 1, H, BF16)
+    got = mdc.mccb_varlen_get_workspace_size(T, 4, H, 3, BF16)
+    assert got == -(-p["workspace_size"] // 256) * 256 + T  # partials, then one byte per token
+    assert mdc.mccb_varlen_forward_get_workspace_size(T, 4, H, 2, BF16) == -(-T // 256) * 256 + T
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "cu", "gx", "gw", "ws"])
+def test_varlen_null_pointer(which):
+    assert vcall(**{which: None}) == NULLPTR
+
+
+@pytest.mark.parametrize("kw", [dict(T=0), dict(T=524289), dict(nseq=0), dict(H=320), dict(taps=5),
+                                dict(taps=0)])
+def test_varlen_shape_out_of_range(kw):
+    assert vcall(**kw) == SHAPE
+
+
+def test_varlen_validation():
+    assert vcall(dt=2) == INVALID
+    assert vcall(cu=CU + 4) == INVALID  # int64 array must be 8-byte aligned
+    assert vcall(x=X + 8) == INVALID
+    assert vcall(wsz=100) == INVALID
+    assert vcall(gx=CU - 64) == INVALID  # gradX overlapping cu_seqlens
+    assert vcall(ws=X + 4096) == INVALID
+    rc = mdc.mccb_varlen_forward(X, W, M, CU, X + 4096, 100, 3, 384, 3, BF16, WS, 1 << 40, None)
+    assert rc == INVALID  # y overlapping x
+    rc = mdc.mccb_varlen_forward(X, W, M, None, GX, 100, 3, 384, 3, BF16, WS, 1 << 40, None)
+    assert rc == NULLPTR

@@ -117,6 +117,12 @@ EDGE = [
     (1000, 2, 1024, "bf16", ("bernoulli", 0.9)),
     (12, 8, 512, "bf16", ("bernoulli", 0.8)),
     (21, 5, 832, "fp16", ("prefix",)),
+    # narrow rows: the block's waves stack along the rows (1, 2 or 4 across)
+    (70, 1, 1024, "bf16", ("bernoulli", 0.8)),
+    (100, 1, 2048, "fp16", ("null",)),
+    (33, 1, 5120, "bf16", ("bernoulli", 0.9)),
+    (65, 1, 384, "bf16", ("prefix",)),
+    (3, 1, 5120, "fp16", ("null",)),
 ]
 
 

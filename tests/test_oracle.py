@@ -166,6 +166,62 @@ def pin_window_autograd_and_adjoint(orc):
             assert abs(lhs - mid) <= 1e-12 * scale and abs(lhs - rhs) <= 1e-12 * scale, (W, S)
 
 
+VARLEN_GOLDEN = os.path.join(HERE, "golden", "varlen_hand_cases.json")
+
+
+def pin_varlen_hand_cases(orc):
+    for c in json.load(open(VARLEN_GOLDEN))["cases"]:
+        cu = np.array(c["cu"], dtype=np.int64)
+        m = None if c["mask"] is None else np.array(c["mask"], dtype=np.uint8)
+        for dtype in ("bf16", "fp16"):
+            tag = f"{c['name']}/{dtype}"
+            x, w = to_bits(c["x"], dtype), to_bits(c["w"], dtype)
+            if c["op"] == "forward":
+                r = orc.forward16_varlen(dtype, x, w, cu, m)
+                exp = np.array(c["y"], np.float64)
+                assert np.array_equal(r["y64"], exp), (tag, r["y64"], exp)
+                assert np.array_equal(from_bits(r["y16"], dtype), exp), tag
+                continue
+            r = orc.backward_varlen(dtype, to_bits(c["gY"], dtype), x, w, cu, m)
+            exp_gx, exp_gw = np.array(c["gX"], np.float64), np.array(c["gW"], np.float64)
+            assert np.array_equal(r["gx64"], exp_gx), (tag, r["gx64"], exp_gx)
+            assert np.array_equal(r["gw64"], exp_gw), (tag, r["gw64"], exp_gw)
+            assert np.array_equal(from_bits(r["gx16"], dtype), exp_gx), tag
+            np.testing.assert_allclose(r["gwrss"] ** 2, np.array(c["gW_sumsq"], float),
+                                       rtol=1e-12, err_msg=tag)
+
+
+def pin_varlen_equals_padded(orc):
+    """The packed layout computes what the padded [S,B,H] layout computes with a per-batch valid
+    prefix mask (lengths = the sequence lengths), on the valid tokens: the same gradX there and the
+    same gradWeight; likewise for the forward. The padded oracle is pinned independently above."""
+    rng = np.random.default_rng(5)
+    for W in (1, 2, 3, 4):
+        for lens in ([5, 1, 3], [7], [2, 0, 6, 4, 1], [1, 1, 1, 1]):
+            B, S, H = len(lens), max(lens), 6
+            T = int(sum(lens))
+            cu = np.cumsum(lens).astype(np.int64)
+            gyp = rng.standard_normal((S, B, H))
+            xp = rng.standard_normal((S, B, H))
+            w = to_bits(rng.standard_normal((W, H)) * 0.5, "bf16")
+            tok = rng.random((S, B)) < 0.8  # an extra per-token mask
+            valid = np.arange(S)[:, None] < np.array(lens)[None, :]
+            gyp16, xp16 = to_bits(gyp, "bf16"), to_bits(xp, "bf16")
+            mask_pad = (valid & tok).T.astype(np.uint8)  # [B,S]
+            order = [(b, i) for b in range(B) for i in range(lens[b])]
+            pack = lambda a: np.stack([a[i, b] for b, i in order]) if order else a[:0, 0]
+            gyv, xv = pack(gyp16), pack(xp16)
+            mv = np.array([tok[i, b] for b, i in order], np.uint8)
+            rp = orc.backward("bf16", gyp16, xp16, w, mask_pad)
+            rv = orc.backward_varlen("bf16", gyv, xv, w, cu, mv)
+            assert np.array_equal(rv["gx64"], pack(rp["gx64"])), (W, lens)
+            scale = np.maximum(rp["gwrss"], 1e-300)
+            assert np.all(np.abs(rv["gw64"] - rp["gw64"]) <= 1e-12 * scale), (W, lens)
+            yp = orc.forward(from_bits(xp16, "bf16"), from_bits(w, "bf16"), mask_pad)
+            yv = orc.forward_varlen(from_bits(xv, "bf16"), from_bits(w, "bf16"), cu, mv)
+            assert np.array_equal(yv, pack(yp)), (W, lens)
+
+
 def pin_call_example(orc):
     # Call example on the page: S=1, B=2, H=192*2, W=3, FLOAT16, every input (and the bool mask)
     # zero-filled. Whatever the print format, the gradients must be zero.
@@ -351,7 +407,8 @@ def pin_codec_encode_bf16(orc):
 
 
 PINS = [pin_hand_cases, pin_forward_hand_cases, pin_window_hand_cases,
-        pin_window_autograd_and_adjoint, pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
+        pin_window_autograd_and_adjoint, pin_varlen_hand_cases, pin_varlen_equals_padded,
+        pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
         pin_codec_decode, pin_codec_roundtrip, pin_codec_encode_fp16, pin_codec_encode_bf16]
 
 
@@ -410,6 +467,10 @@ MUTANTS = [
     ("gradX window stuck at 3 taps",
      "for (int k = 0; k < W; ++k) {\n                    acc += grad_y_masked",
      "for (int k = 0; k < W && k < 3; ++k) {\n                    acc += grad_y_masked"),
+    ("varlen gradX reads across a sequence end", "if (r >= end) break;", "if (r >= T) break;"),
+    ("varlen forward reads before a sequence start", "if (src < start) continue;",
+     "if (src < 0) continue;"),
+    ("varlen gradWeight crosses sequences", "if (r >= end) continue;", "if (r >= T) continue;"),
     ("forward window stuck at 3 taps",
      "for (int k = 0; k < W; ++k) {\n                    const int64_t src",
      "for (int k = 0; k < W && k < 3; ++k) {\n                    const int64_t src"),
