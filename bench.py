@@ -111,6 +111,59 @@ def cpu_baseline(wl, gy, x, w, m, seconds: float, rows_per_chunk: int = 64) -> d
     }
 
 
+def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list:
+    """Backward and forward of every workload, each call timed on its own between HIP events,
+    after reading a 1 GiB scratch buffer so that no input is left in the 256 MB Infinity Cache or
+    the L2s (the small workloads would otherwise run from cache). The flush reads rather than
+    writes, so no dirty lines are left to be written back during the timed call. Median and
+    minimum."""
+    import statistics
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_call(fn):
+        times = []
+        for r in range(reps + 2):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(e0.elapsed_time(e1))
+        return statistics.median(times), min(times)
+
+    rows = []
+    for wlc in workloads:
+        gy_c = wls.full_tensor(wlc, wls.STREAM_GY, dev)
+        x_c = wls.full_tensor(wlc, wls.STREAM_X, dev)
+        w_c, m_c = wls.weight_tensor(wlc, dev), wls.mask_tensor(wlc, dev)
+        gx_c, gw_c, y_c = torch.empty_like(gy_c), torch.empty_like(w_c), torch.empty_like(x_c)
+        ws_c = mdc.workspace_for(wlc.S, wlc.B, wlc.H, gy_c.dtype, dev)
+        torch.cuda.synchronize()
+        b_med, b_min = per_call(lambda: mdc.backward(gy_c, x_c, w_c, m_c, gradX=gx_c,
+                                                     gradWeight=gw_c, workspace=ws_c,
+                                                     stream=stream))
+        f_med, f_min = per_call(lambda: mdc.forward(x_c, w_c, m_c, y=y_c, stream=stream))
+        b_alg = wlc.algorithmic_bytes()
+        f_alg = 4 * wlc.N + (wlc.B * wlc.S if m_c is not None else 0) + 3 * wlc.H * 2
+        rows.append({
+            "workload": wlc.describe(),
+            "backward": {"median_ms": round(b_med, 5), "min_ms": round(b_min, 5),
+                         "gbs": round(b_alg / (b_med * 1e-3) / 1e9, 1),
+                         "pct_of_hbm_peak": round(100 * b_alg / (b_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+            "forward": {"median_ms": round(f_med, 5), "min_ms": round(f_min, 5),
+                        "gbs": round(f_alg / (f_med * 1e-3) / 1e9, 1),
+                        "pct_of_hbm_peak": round(100 * f_alg / (f_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+        })
+        log(f"config {wlc.name}: backward {b_med:.4f} ms, forward {f_med:.4f} ms")
+        del gy_c, x_c, w_c, m_c, gx_c, gw_c, y_c, ws_c
+        torch.cuda.empty_cache()
+    del flush
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +181,9 @@ def main() -> int:
                     help="skip timing both ops with 2- and 4-tap windows")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip timing both ops on the packed variable-length layout")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-call timing of every workload")
+    ap.add_argument("--config-reps", type=int, default=15)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -341,6 +397,12 @@ def main() -> int:
         cpu = cpu_baseline(wl, gy, x, w, m, args.cpu_seconds)
         log(f"cpu baseline {cpu['value']} GB/s on {cpu['cores']} threads")
 
+    configs = None
+    if not args.no_configs:
+        del gy, x, gx, ws, m
+        torch.cuda.empty_cache()
+        configs = time_all_configs(torch, mdc, WORKLOADS, wls, dev, stream, args.config_reps)
+
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -363,6 +425,7 @@ def main() -> int:
         "strided": strided,
         "taps": taps,
         "varlen": varlen,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
     return 0

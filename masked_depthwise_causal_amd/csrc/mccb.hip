@@ -573,15 +573,20 @@ __device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
 // VARLEN (packed variable-length layout, B = 1): `behind[i]` holds the number of rows before row i
 // that belong to its sequence; the window of row i uses only those.
 //
-// `cw` (1, 2, 4 or kFwdWaves, chosen by the host) is how many of the block's waves sit side by side
-// across the columns; the rest stack along the rows, so a block covers (kFwdWaves / cw) * kFwdRows
-// rows x cw * kWave * kFwdVec columns. Narrow rows (the packed layout's H columns, or a small
+// cw = 2^cw_log2 (1, 2, 4 or kFwdWaves, chosen by the host) is how many of the block's waves sit
+// side by side across the columns; the rest stack along the rows, so a block covers
+// (kFwdWaves / cw) * kFwdRows rows x cw * kWave * kFwdVec columns. Narrow rows (the packed layout's H columns, or a small
 // B*H) use fewer columns per block instead of leaving lanes idle.
+// Register budget: 4 wavefronts per SIMD (at most 128 VGPRs) for windows of up to 3 taps; the
+// 16-byte lanes of a 4-tap window, or a 3-tap window with per-row sequence limits, need more.
+constexpr int fwd_waves_per_simd(int w, bool varlen) { return (w > 3 || (varlen && w == 3)) ? 3 : 4; }
+
 template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
+    __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(W, VARLEN))))
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
-             int64_t H, int64_t n_ct, int cw, InStrides st,
+             int64_t H, int64_t n_ct, int cw_log2, InStrides st,
              const uint8_t *__restrict__ behind = nullptr) {
     constexpr int L = W - 1;  // look-back rows
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
@@ -590,16 +595,15 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     const int64_t rt = blockIdx.x / n_ct;  // row tile
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wc = wave % cw, wr = wave / cw;  // the wave's column slot and row slot
+    const int wc = wave & ((1 << cw_log2) - 1), wr = wave >> cw_log2;  // column slot, row slot
     const int64_t C = B * H;
-    const int64_t c0 = (ct * cw + wc) * (int64_t)(kWave * kFwdVec) + lane * kFwdVec;
+    const int64_t c0 = ((ct << cw_log2) + wc) * (int64_t)(kWave * kFwdVec) + lane * kFwdVec;
     if (c0 >= C) return;  // no barrier below: lanes past the last column just leave
     const int64_t CV = C / kFwdVec;  // lane vectors per row (C is a multiple of 64)
     const int64_t v = c0 / kFwdVec;
     const int64_t h0 = c0 % H;  // the lane's kFwdVec channels share one batch: H % 64 == 0
     const int64_t j = c0 / H;
-    const int64_t r0 = (rt * (kFwdWaves / cw) + wr) * kFwdRows;
-    if (r0 >= S) return;
+    const int64_t r0 = (rt * (kFwdWaves >> cw_log2) + wr) * kFwdRows;  // may be >= S: rows guarded
 
     // x rows r0-L .. r0+kFwdRows-1; rows outside [0, S) are zero
     fvec_t xr[kFwdRows + L];
@@ -832,7 +836,7 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
 // lanes (all kFwdWaves when B*H is large), and stack along the rows otherwise.
 struct FwdPlan {
     int64_t n_ct, n_rt, rows, cols;
-    int cw;
+    int cw, cw_log2;
 };
 
 FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
@@ -847,6 +851,8 @@ FwdPlan make_fwd_plan(int64_t S, int64_t B, int64_t H) {
             break;
         }
     }
+    f.cw_log2 = 0;
+    while ((1 << f.cw_log2) < f.cw) ++f.cw_log2;
     f.cols = f.cw * wave_cols;
     f.rows = (int64_t)(kFwdWaves / f.cw) * kFwdRows;
     f.n_ct = (C + f.cols - 1) / f.cols;
@@ -864,7 +870,7 @@ hipError_t launch_fwd(int64_t S, int64_t B, int64_t H, int W, const void *x, con
 #define MCCB_FWD(M, T, TAPS)                                                                      \
     hipLaunchKernelGGL((mccb_fwd<DT, M, T, TAPS>), grid, block, MCCB_FWD_LDS, st,                \
                        (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, S, B, H, f.n_ct,  \
-                       f.cw, is)
+                       f.cw_log2, is)
 #define MCCB_FWD_W(TAPS)                                                                          \
     if (mask) {                                                                                   \
         if (strided) MCCB_FWD(true, true, TAPS); else MCCB_FWD(true, false, TAPS);                \
@@ -1062,7 +1068,7 @@ hipError_t launch_varlen_fwd(int64_t T, int64_t H, int W, const void *x, const v
 #define MCCB_VLF(M, TAPS)                                                                         \
     hipLaunchKernelGGL((mccb_fwd<DT, M, false, TAPS, true>), grid, block, MCCB_FWD_LDS, st,      \
                        (const fvec_t *)x, (const fvec_t *)w, mask, (fvec_t *)y, T, (int64_t)1, H, \
-                       f.n_ct, f.cw, is, behind)
+                       f.n_ct, f.cw_log2, is, behind)
 #define MCCB_VLF_W(TAPS)                                                                          \
     if (mask) MCCB_VLF(true, TAPS); else MCCB_VLF(false, TAPS);
     switch (W) {

@@ -137,3 +137,19 @@ def test_generator_same_bits_on_gpu_and_cpu():
     hs = torch.tensor([0, 5, 511])
     assert torch.equal(wls.column_tensor(small, wls.STREAM_GY, hs).view(torch.int16),
                        g_cpu[:, :, hs].contiguous().view(torch.int16))
+
+
+def test_max_sequence_length_sampled():
+    """The longest sequence the constraints allow (B*S = 524288 with B = 1), narrowest H."""
+    wl = custom(524288, 1, 384, "bf16", ("bernoulli", 0.9), seed=524)
+    inputs = gpu_inputs(wl)
+    gx, gw = gpu_run(wl, inputs)
+    hs = sample_channels(wl, n_random=6, seed=5)
+    announce(f"compare {wl.name}: sampled channels")
+    compare_columns(wl, gx, gw, hs)
+    compare_rows(wl, gx, sample_rows(wl, plan_of(wl), seed=5))
+    del gx, gw
+    from .test_forward import compare_columns as fwd_columns
+    from .test_forward import gpu_forward
+    y = gpu_forward(wl, (inputs[1], inputs[2], inputs[3]))
+    fwd_columns(wl, y, hs)
