@@ -414,9 +414,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": "f64",  # arithmetic: every sum is an fp64 FMA chain; storage is config.storage_dtype
         "data": "synthetic",
         "config": {"workload": wl.describe(), "S": wl.S, "B": wl.B, "H": wl.H,
+                   "storage_dtype": wl.dtype,
                    "algorithmic_bytes": alg, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "copy_ceiling_gbs": ceiling},
         "roofline": roofline,

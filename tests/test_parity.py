@@ -67,6 +67,7 @@ EDGE = [
     (16, 32, 384, "fp16", ("all_false",)),
     (8, 1, 24576, "bf16", ("bernoulli", 0.9)),
     (3, 2, 24576, "fp16", ("null",)),
+    (4, 32, 24576, "bf16", ("bernoulli", 0.7)),  # the widest row: B*H = 786432
 ]
 
 
