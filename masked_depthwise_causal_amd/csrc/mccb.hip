@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "mccb.h"
@@ -63,6 +64,9 @@
 #endif
 #ifndef MCCB_WAVES_PER_SIMD
 #define MCCB_WAVES_PER_SIMD 4  // occupancy the fused kernel is compiled for (caps its VGPRs)
+#endif
+#ifndef MCCB_NARROW_COL_GROUPS
+#define MCCB_NARROW_COL_GROUPS 2  // column groups of the variants compiled for one wave less
 #endif
 #ifndef MCCB_EXACT_GRADX
 #define MCCB_EXACT_GRADX 1  // 1: gradX correctly rounded from fp64; 0: fp64 -> fp32 -> dtype
@@ -240,7 +244,8 @@ __device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: mask + gradX + gradWeight partials in one HBM pass, for a window of W taps (the
 // look-ahead is W-1 rows).
-// grid.x = n_col_blocks * n_strips (column block fastest), block = kColGroups * kRing waves.
+// grid.x = n_col_blocks * n_strips (column block fastest), block = CG * kRing waves with CG =
+// fused_col_groups(STRIDED, W) column groups.
 // Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + W - 1) mask bytes.
 // Workspace: fp64 partials [n_strips][W][C].
 // ---------------------------------------------------------------------------------------------
@@ -257,16 +262,25 @@ struct InStrides {
 
 // Register budget: the strided variant keeps a second lane offset and row stride, and a wider
 // window keeps more fp64 state; such variants are compiled for one wavefront less per SIMD so that
-// they do not spill.
+// they do not spill, and their blocks are narrower (fewer column groups) so that a CU still holds
+// two or more of them: with one wavefront less per SIMD a CU has room for only one full block.
+// The block shape does not enter the arithmetic: each column's partial is the same sum of the
+// same ring waves' turns whatever the number of column groups beside it.
+constexpr bool fused_narrow(bool strided, int w) { return (strided && w >= 3) || w > 3; }
 constexpr int fused_waves_per_simd(bool strided, int w) {
-    return (strided || w > 3) ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD;
+    return fused_narrow(strided, w) ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD;
 }
+constexpr int fused_col_groups(bool strided, int w) {
+    return fused_narrow(strided, w) ? MCCB_NARROW_COL_GROUPS : kColGroups;
+}
+static_assert(MCCB_NARROW_COL_GROUPS >= 1 && MCCB_NARROW_COL_GROUPS <= kColGroups,
+              "narrow blocks must not be wider than the full ones");
 
 // VARLEN (packed variable-length layout, B = 1): `ahead[i]` holds the number of rows i, i+1, ...
 // that belong to row i's sequence (at least 1); the stencil of row i uses only those. The bytes of
 // the strip are staged in LDS after the mask's `lim_lds` bytes.
 template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
-__global__ void __launch_bounds__(kBlockWaves *kWave)
+__global__ void __launch_bounds__(fused_col_groups(STRIDED, W) * kRing * kWave)
     __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(STRIDED, W))))
     mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
                    const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
@@ -274,15 +288,18 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
                    int64_t rows_per_strip, int64_t n_col_blocks, InStrides st,
                    const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
     constexpr int L = W - 1;  // look-ahead rows
+    constexpr int CG = fused_col_groups(STRIDED, W);  // column groups side by side
+    constexpr int BW = CG * kRing;                     // waves per block
+    constexpr int BC = CG * kGroupCols;                // columns per block
     extern __shared__ uint8_t smask[];
-    __shared__ f64x2 red[kBlockWaves][kWave * kVec / 2];
+    __shared__ f64x2 red[BW][kWave * kVec / 2];
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane of a wave; saying so keeps everything derived from
     // it (row ranges, row addresses) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int ring = wave / kColGroups;  // position along rows
-    const int group = wave % kColGroups;  // column group
+    const int ring = wave / CG;  // position along rows
+    const int group = wave % CG;  // column group
     const int64_t C = B * H;
     const int64_t CV = C / kVec;  // lane vectors per row
     const int64_t col_block = blockIdx.x % n_col_blocks;
@@ -291,7 +308,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     const int64_t rs1 = (rs0 + rows_per_strip < S) ? rs0 + rows_per_strip : S;
 
     // Lanes past the last column load a valid column (the last one) and store nothing.
-    const int64_t v_raw = (col_block * kColGroups + group) * kWave + lane;
+    const int64_t v_raw = (col_block * CG + group) * kWave + lane;
     const bool active = v_raw < CV;
     const int64_t v = active ? v_raw : CV - 1;
     const int64_t c = v * kVec;
@@ -300,8 +317,8 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 
     int moff = 0;  // offset of this lane's batch in the staged mask
     if constexpr (HAS_MASK) {
-        const int64_t c_first = col_block * kBlockCols;
-        const int64_t c_last = (c_first + kBlockCols < C ? c_first + kBlockCols : C) - 1;
+        const int64_t c_first = col_block * BC;
+        const int64_t c_last = (c_first + BC < C ? c_first + BC : C) - 1;
         const int64_t j_first = c_first / H;
         const int nj = (int)(c_last / H - j_first + 1);
         const int span = (int)(rows_per_strip + L);
@@ -356,7 +373,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
     const int64_t row_bytes = C * 2;
     const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
     // STRIDED: the block's first batch goes into the uniform base, the lane keeps the rest
-    const int64_t jb = (col_block * kBlockCols) / H;
+    const int64_t jb = (col_block * BC) / H;
     const char *gy_base = reinterpret_cast<const char *>(gy) + (STRIDED ? jb * st.gy_batch * 2 : 0);
     const char *x_base = reinterpret_cast<const char *>(x) + (STRIDED ? jb * st.x_batch * 2 : 0);
     const int64_t gy_rb = STRIDED ? st.gy_row * 2 : row_bytes;
@@ -467,7 +484,7 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
 
     // gradWeight partials of the strip: for each column group add its kRing waves in a fixed
     // order (ring position 0 first).
-    const int64_t col0 = col_block * kBlockCols;
+    const int64_t col0 = col_block * BC;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         __syncthreads();
@@ -476,11 +493,11 @@ __global__ void __launch_bounds__(kBlockWaves *kWave)
             red[wave][lane * (kVec / 2) + p] = f64x2{a[k][2 * p], a[k][2 * p + 1]};
         __syncthreads();
         const double *flat = reinterpret_cast<const double *>(&red[0][0]);
-        for (int t = threadIdx.x; t < kBlockCols; t += blockDim.x) {
+        for (int t = threadIdx.x; t < BC; t += blockDim.x) {
             const int g = t / kGroupCols, within = t - g * kGroupCols;
             double s = flat[g * kGroupCols + within];
 #pragma unroll
-            for (int q = 1; q < kRing; ++q) s += flat[(q * kColGroups + g) * kGroupCols + within];
+            for (int q = 1; q < kRing; ++q) s += flat[(q * CG + g) * kGroupCols + within];
             const int64_t col = col0 + t;
             if (col < C) ws[(strip * W + k) * C + col] = s;
         }
@@ -575,15 +592,15 @@ __device__ static inline void widen_f(const fvec_t q, double (&d)[kFwdVec]) {
 //
 // cw = 2^cw_log2 (1, 2, 4 or kFwdWaves, chosen by the host) is how many of the block's waves sit
 // side by side across the columns; the rest stack along the rows, so a block covers
-// (kFwdWaves / cw) * kFwdRows rows x cw * kWave * kFwdVec columns. Narrow rows (the packed layout's H columns, or a small
-// B*H) use fewer columns per block instead of leaving lanes idle.
+// (kFwdWaves / cw) * kFwdRows rows x cw * kWave * kFwdVec columns. Narrow rows (the packed
+// layout's H columns, or a small B*H) use fewer columns per block instead of leaving lanes idle.
 // Register budget: 4 wavefronts per SIMD (at most 128 VGPRs) for windows of up to 3 taps; the
-// 16-byte lanes of a 4-tap window, or a 3-tap window with per-row sequence limits, need more.
-constexpr int fwd_waves_per_simd(int w, bool varlen) { return (w > 3 || (varlen && w == 3)) ? 3 : 4; }
+// 16-byte lanes of a 4-tap window need more.
+constexpr int fwd_waves_per_simd(int w) { return w > 3 ? 3 : 4; }
 
 template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
 __global__ void __launch_bounds__(kFwdWaves *kWave)
-    __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(W, VARLEN))))
+    __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(W))))
     mccb_fwd(const fvec_t *__restrict__ x, const fvec_t *__restrict__ w,
              const uint8_t *__restrict__ mask, fvec_t *__restrict__ y, int64_t S, int64_t B,
              int64_t H, int64_t n_ct, int cw_log2, InStrides st,
@@ -620,22 +637,42 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
         }
         xr[u] = q;
     }
-    double wt[W][kFwdVec];
+    // Weights: fp64 copies take 2*W*kFwdVec registers for the whole tile. The 4-tap and the
+    // packed-layout instantiations, which need the room, keep them in fp32 (exact for 16-bit
+    // values) and widen them at each use instead; the others keep fp64 copies, which measured
+    // faster for them.
+    constexpr bool kNarrowW = W > 3 || VARLEN;
+    typedef typename std::conditional<kNarrowW, float, double>::type wt_t;
+    wt_t wt[W][kFwdVec];
 #pragma unroll
-    for (int k = 0; k < W; ++k) widen_f<DT>(w[(k * H + h0) / kFwdVec], wt[k]);
+    for (int k = 0; k < W; ++k) {
+        const fvec_t q = w[(k * H + h0) / kFwdVec];
+#pragma unroll
+        for (int p = 0; p < kFwdWords; ++p) {
+            float lo, hi;
+            Fmt<DT>::unpack(q[p], lo, hi);
+            wt[k][2 * p] = lo;
+            wt[k][2 * p + 1] = hi;
+        }
+    }
     uint8_t keep[kFwdRows];
 #pragma unroll
     for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
-    int first[kFwdRows];  // first window position inside the row's sequence
-#pragma unroll
-    for (int u = 0; u < kFwdRows; ++u) first[u] = 0;
+    // VARLEN: rows of the tile whose window reaches into another sequence. If the tile's last row
+    // has at least kFwdRows-1+L earlier rows in its sequence, no row of the tile does, and the
+    // tile takes the unlimited form (a uniform branch; only tiles at sequence starts do not).
+    bool limited = false;
     if constexpr (VARLEN) {
-#pragma unroll
-        for (int u = 0; u < kFwdRows; ++u) {
-            const int b = (r0 + u < S) ? (int)behind[r0 + u] : L;
-            first[u] = L - (b < L ? b : L);
-        }
+        const int64_t last = r0 + kFwdRows - 1;
+        limited = __builtin_amdgcn_readfirstlane(
+                      (last < S && behind[last] >= kFwdRows - 1 + L) ? 0 : 1) != 0;
     }
+    // first window position inside row r0+u's sequence (limited tiles only): window rows before
+    // it belong to an earlier sequence
+    auto first_of = [&](int u) -> int {
+        const int b = (r0 + u < S) ? (int)behind[r0 + u] : L;
+        return __builtin_amdgcn_readfirstlane(L - (b < L ? b : L));
+    };
     if (HAS_MASK) {
         const uint8_t *mrow = mask + j * st.m_batch + r0 * st.m_row;
 #pragma unroll
@@ -649,14 +686,33 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     for (int u = 0; u < kFwdRows; ++u) {
         const int64_t row = r0 + u;
         widen_f<DT>(xr[u + L], win[L]);
+        if (VARLEN && limited) {
+            // Window rows of an earlier sequence count as zero: clear them here, once; the window
+            // only slides forward, so later rows of this sequence never see them either.
+            const int first = first_of(u);
+            if (first > 0) {
+#pragma unroll
+                for (int k = 0; k < L; ++k)
+                    if (k < first)
+#pragma unroll
+                        for (int e = 0; e < kFwdVec; ++e) win[k][e] = 0.0;
+            }
+        }
+        // fp32 weights: an empty asm that "changes" them each row, so that their widening is
+        // redone here instead of being hoisted into fp64 copies that live through the tile.
+        if constexpr (kNarrowW) {
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+#pragma unroll
+                for (int e = 0; e < kFwdVec; ++e) asm volatile("" : "+v"(wt[k][e]));
+        }
         float out[kFwdVec];
 #pragma unroll
         for (int e = 0; e < kFwdVec; ++e) {
             // y[i] = sum_k w[k] x[i-L+k], in k order, exact in fp64, rounded once
-            double s = ((!VARLEN || 0 >= first[u]) ? win[0][e] : 0.0) * wt[0][e];
+            double s = win[0][e] * (double)wt[0][e];
 #pragma unroll
-            for (int k = 1; k < W; ++k)
-                s = __builtin_fma((!VARLEN || k >= first[u]) ? win[k][e] : 0.0, wt[k][e], s);
+            for (int k = 1; k < W; ++k) s = __builtin_fma(win[k][e], (double)wt[k][e], s);
             out[e] = keep[u] ? round_to_odd_f32(s) : 0.0f;
         }
         fvec_t r;
@@ -791,19 +847,29 @@ struct Profile {
     std::vector<hipEvent_t> ev;  // 3 per call: before kernel 1, between, after kernel 2
 } g_prof;
 
+// Column blocks of a fused-kernel variant with `cg` column groups. The strips (and with them the
+// gradWeight summation order) come from the plan alone; only the launch's width varies.
+int64_t col_blocks(int64_t C, int cg) {
+    const int64_t cols = (int64_t)cg * kGroupCols;
+    return (C + cols - 1) / cols;
+}
+
 template <int DT>
 hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, const uint8_t *mask,
                   void *gx, void *gw, void *ws, hipStream_t st, hipEvent_t *ev,
                   const InStrides &is, bool strided) {
-    const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
-    const dim3 block1(kBlockWaves * kWave);
     const size_t lds_floor = MCCB_LDS_FLOOR;
     const size_t lds = mask ? (p.mask_lds > lds_floor ? p.mask_lds : lds_floor) : lds_floor;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
 #define MCCB_FUSED(M, T, TAPS)                                                                    \
-    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS>), grid1, block1, lds, st,                 \
-                       (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx,  \
-                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, p.n_col_blocks, is)
+    do {                                                                                          \
+        constexpr int cg = fused_col_groups(T, TAPS);                                             \
+        const int64_t ncb = col_blocks(p.C, cg);                                                  \
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS>), dim3((unsigned)(ncb * p.n_strips)),  \
+                           dim3(cg * kRing * kWave), lds, st, (const vec_t *)gy, (const vec_t *)x, \
+                           (const vec_t *)w, mask, (vec_t *)gx, (double *)ws, p.S, p.B, p.H,      \
+                           p.rows_per_strip, ncb, is);                                            \
+    } while (0)
 #define MCCB_FUSED_W(TAPS)                                                                        \
     if (mask) {                                                                                   \
         if (strided) MCCB_FUSED(true, true, TAPS); else MCCB_FUSED(true, false, TAPS);            \
@@ -1021,17 +1087,20 @@ hipError_t launch_varlen_bwd(const Plan &p, const void *gy, const void *x, const
                        nseq, T, ahead, (uint8_t *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid1((unsigned)(p.n_col_blocks * p.n_strips));
-    const dim3 block1(kBlockWaves * kWave);
     const int span = (int)(p.rows_per_strip + p.W - 1);
     const int lim_lds = mask ? (int)p.mask_lds : 0;
     const size_t lds = (size_t)lim_lds + (size_t)span;
     const InStrides is{p.H, p.H, p.H, p.H, T, 1};
 #define MCCB_VL(M, TAPS)                                                                          \
-    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, false, TAPS, true>), grid1, block1, lds, st,       \
-                       (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask, (vec_t *)gx,  \
-                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, p.n_col_blocks, is, ahead,  \
-                       lim_lds)
+    do {                                                                                          \
+        constexpr int cg = fused_col_groups(false, TAPS);                                         \
+        const int64_t ncb = col_blocks(p.C, cg);                                                  \
+        hipLaunchKernelGGL((mccb_fused_bwd<DT, M, false, TAPS, true>),                            \
+                           dim3((unsigned)(ncb * p.n_strips)), dim3(cg * kRing * kWave), lds, st, \
+                           (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask,           \
+                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip, ncb, is,   \
+                           ahead, lim_lds);                                                       \
+    } while (0)
 #define MCCB_VL_W(TAPS)                                                                           \
     if (mask) MCCB_VL(true, TAPS); else MCCB_VL(false, TAPS);
     switch (p.W) {
