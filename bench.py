@@ -111,6 +111,64 @@ def cpu_baseline(wl, gy, x, w, m, seconds: float, rows_per_chunk: int = 64) -> d
     }
 
 
+def cpu_single_thread(workloads, seconds: float, rows_per_chunk: int = 64) -> list:
+    """The oracle on one thread, on bounded samples of the small workloads (0-2): consecutive
+    64-row chunks, regenerated on the CPU, until `seconds` of oracle time per workload."""
+    import torch
+
+    import oracle
+    from synth import workloads as wls
+
+    orc = oracle.get()
+    n0 = orc.num_threads()
+    out = []
+    try:
+        orc.set_num_threads(1)
+        for wl in workloads:
+            w16 = wls.bits(wls.weight_tensor(wl, "cpu"))
+            mfull = wls.mask_tensor(wl, "cpu")
+            elapsed, rows, chunks = 0.0, 0, 0
+            while elapsed < seconds and rows < wl.S:
+                r1 = min(rows + rows_per_chunk, wl.S)
+                rr = torch.arange(rows, r1, dtype=torch.int64)
+                gyc = wls.bits(wls.row_tensor(wl, wls.STREAM_GY, rr))
+                xc = wls.bits(wls.row_tensor(wl, wls.STREAM_X, rr))
+                mc = None if mfull is None else mfull[:, rows:r1].contiguous().numpy()
+                t0 = time.perf_counter()
+                orc.backward(wl.dtype, gyc, xc, w16, mc, want_gx64=False)
+                elapsed += time.perf_counter() - t0
+                chunks += 1
+                rows = r1
+            elems = rows * wl.B * wl.H
+            alg = 3 * elems * 2 + (rows * wl.B if mfull is not None else 0) + chunks * 12 * wl.H
+            out.append({"workload": wl.describe(), "value": round(alg / elapsed / 1e9, 4),
+                        "unit": "GB/s", "cores": 1,
+                        "sample": (f"rows 0..{rows - 1} of {wl.S} in {chunks} chunk(s) of up to "
+                                   f"{rows_per_chunk} rows, {elapsed:.2f} s of oracle time")})
+    finally:
+        orc.set_num_threads(n0)
+    return out
+
+
+def stream_ceiling(torch, a, b, stream, reps: int = 20) -> float:
+    """GB/s of torch's elementwise a + b into a third tensor (2 reads, 1 write of the same shape
+    as the backward's streams), timed between events on `stream`."""
+    c = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        torch.add(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del c
+    torch.cuda.empty_cache()
+    return 3 * a.numel() * a.element_size() / (ms * 1e-3) / 1e9
+
+
 def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list:
     """Backward and forward of every workload, each call timed on its own between HIP events,
     after reading a 1 GiB scratch buffer so that no input is left in the 256 MB Infinity Cache or
@@ -172,6 +230,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None,
                     help="index into synth.WORKLOADS (default: the B*S=512K H=5120 workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-single-seconds", type=float, default=1.5,
+                    help="oracle time per workload for the single-thread samples (workloads 0-2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-forward", action="store_true", help="skip timing the forward")
@@ -386,16 +446,20 @@ def main() -> int:
         del gy_v, x_v, gx_v, gw_v, y_v, ws_b, ws_f
         torch.cuda.empty_cache()
 
-    ceiling = None
+    ceiling = stream_gbs = None
     if not args.no_ceiling:
         ceiling = round(copy_ceiling(torch, dev), 1)
         log(f"copy ceiling {ceiling} GB/s")
+        stream_gbs = round(stream_ceiling(torch, gy, x, stream), 1)
+        log(f"read-2/write-1 streaming ceiling (torch add) {stream_gbs} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, gy, x, w, m, args.cpu_seconds)
         log(f"cpu baseline {cpu['value']} GB/s on {cpu['cores']} threads")
+        cpu["single_thread"] = cpu_single_thread(WORKLOADS[:3], args.cpu_single_seconds)
+        log("cpu single thread: " + ", ".join(str(r["value"]) for r in cpu["single_thread"]))
 
     configs = None
     if not args.no_configs:
@@ -419,7 +483,9 @@ def main() -> int:
         "config": {"workload": wl.describe(), "S": wl.S, "B": wl.B, "H": wl.H,
                    "storage_dtype": wl.dtype,
                    "algorithmic_bytes": alg, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "copy_ceiling_gbs": ceiling},
+                   "copy_ceiling_gbs": ceiling, "stream_ceiling_gbs": stream_gbs,
+                   "pct_of_stream_ceiling": (round(100 * value / stream_gbs, 2)
+                                             if stream_gbs else None)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "forward": fwd,

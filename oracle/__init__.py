@@ -50,6 +50,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_encode.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_backward.argtypes = [ctypes.c_int, i64, i64, i64, _u16p, _u16p, _u16p, _u8p,
                                     _f64p, _u16p, _f64p, _f64p, _u16p]
     lib.oracle_backward.restype = ctypes.c_int
@@ -100,6 +102,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """OpenMP threads of the following calls (timing only: results do not depend on it)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     # -- the backward -----------------------------------------------------------------------------
     def backward(self, dtype: str, gY: np.ndarray, x: np.ndarray, w: np.ndarray,

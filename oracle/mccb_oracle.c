@@ -131,6 +131,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the following calls (n >= 1); the results do not depend on it: each thread owns
+   whole channels and sums them in the same order. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------------------
  * The backward (function description section, all three equations).
  * --------------------------------------------------------------------------------------------- */

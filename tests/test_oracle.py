@@ -440,6 +440,22 @@ def test_result_independent_of_thread_count(tmp_path):
     assert np.array_equal(outs[0], outs[1])
 
 
+def test_set_num_threads_keeps_results(orc):
+    """The thread-count setter (used to time the oracle on one thread) changes no result."""
+    gy, x, w, m = random_case(23, 2, 40, "fp16", ("bernoulli", 0.6), seed=8)
+    n0 = orc.num_threads()
+    try:
+        orc.set_num_threads(1)
+        assert orc.num_threads() == 1
+        a = orc.backward("fp16", gy, x, w, m)
+        orc.set_num_threads(max(n0, 3))
+        b = orc.backward("fp16", gy, x, w, m)
+    finally:
+        orc.set_num_threads(n0)
+    assert np.array_equal(a["gx64"], b["gx64"]) and np.array_equal(a["gw64"], b["gw64"])
+    assert np.array_equal(a["gx16"], b["gx16"]) and np.array_equal(a["gw16"], b["gw16"])
+
+
 # -- planted mistakes ------------------------------------------------------------------------------
 MUTANTS = [
     ("tap orientation reversed", "wd[(W - 1 - k) * H + h]", "wd[k * H + h]"),

@@ -87,6 +87,30 @@ def test_varlen_small_full(lengths, H, dtype, W, p):
     check_gradx(bits16(y), refy["y16"], f"varlen {lengths} forward")
 
 
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_varlen_sequence_starts_at_every_tile_offset(W):
+    """Sequence starts at every offset inside a wave's 8-row tile (and on tile edges), with
+    lengths around the look-back: the forward takes the unlimited form only for tiles whose last
+    row has at least 7 + W - 1 earlier rows in its sequence, and clears the window at each start."""
+    lengths = []
+    for off in range(8):
+        lengths += [8 + off, 1, W - 1, W, 16 - off]
+    lengths = [v for v in lengths if v > 0]
+    H = 640
+    wl = custom(max(lengths), len(lengths), H, "bf16", ("null",), seed=900 + W, W=W)
+    gy, x, w, cu, m = packed_inputs(wl, lengths, "cuda", 0.9)
+    T = int(sum(lengths))
+    announce(f"mccb_varlen_forward/backward tile offsets T={T} nseq={len(lengths)} W={W}")
+    gx, gw = mdc.varlen_backward(gy, x, w, cu, m)
+    y = mdc.varlen_forward(x, w, cu, m)
+    torch.cuda.synchronize()
+    ref = oracle_backward(wl, lengths, gy, x, w, m)
+    check_gradx(bits16(gx), ref["gx16"], f"tile offsets W={W} gradX")
+    check_gradw(bits16(gw), ref, "bf16", f"tile offsets W={W} gradWeight")
+    refy = oracle_forward(wl, lengths, x, w, m)
+    check_gradx(bits16(y), refy["y16"], f"tile offsets W={W} forward")
+
+
 def test_varlen_matches_padded_prefix_mask():
     """Packed layout vs the padded layout with each batch's mask cut at its length: the same
     gradX on the valid tokens, bit for bit (both are correctly rounded)."""
