@@ -12,7 +12,8 @@
 // So the whole op is a 3-tap stencil down the rows of that matrix plus a column-group reduction.
 //
 // Kernel 1 (fused): a lane owns kVec consecutive columns (one 4-byte load per row). A block is
-// kColGroups x kRing wavefronts: kColGroups waves side by side cover kColGroups*64*kVec contiguous
+// kColGroups x kRing wavefronts (fewer column groups for the instantiations that need more
+// registers): kColGroups waves side by side cover kColGroups*64*kVec contiguous
 // columns, and kRing waves stacked on each column group take the rows of the block's strip round
 // robin, kTurnRows rows each per round, with a block barrier per round. So at any moment a block
 // reads one contiguous stretch of each of kRing*kTurnRows consecutive rows, and all its waves
