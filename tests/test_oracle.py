@@ -490,6 +490,21 @@ MUTANTS = [
     ("forward window stuck at 3 taps",
      "for (int k = 0; k < W; ++k) {\n                    const int64_t src",
      "for (int k = 0; k < W && k < 3; ++k) {\n                    const int64_t src"),
+    ("varlen gradX ignores the token mask",
+     "mask[r] != 0) ? 1.0 : 0.0;\n                    acc += m * gyd",
+     "mask[r] != 0) ? 1.0 : 1.0;\n                    acc += m * gyd"),
+    ("varlen gradX masks by the output token",
+     "if (r >= end) break;\n                    const double m = (mask == NULL || mask[r] != 0)",
+     "if (r >= end) break;\n                    const double m = (mask == NULL || mask[t] != 0)"),
+    ("varlen gradWeight ignores the token mask",
+     "mask[r] != 0) ? 1.0 : 0.0;\n                    const double term",
+     "mask[r] != 0) ? 1.0 : 1.0;\n                    const double term"),
+    ("varlen forward ignores the token mask",
+     "mask[t] != 0) ? 1.0 : 0.0;\n                y[t * H + h] = m * acc;",
+     "mask[t] != 0) ? 1.0 : 1.0;\n                y[t * H + h] = m * acc;"),
+    ("encoder saturates on overflow",
+     "if (field >= (double)inf_field) return (uint16_t)(sign | inf_field);",
+     "if (field >= (double)inf_field) return (uint16_t)(sign | (inf_field - 1u));"),
 ]
 
 
