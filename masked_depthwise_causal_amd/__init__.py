@@ -184,6 +184,14 @@ def _strides(gradY, x, weight, mask) -> Strides | None:
     return st
 
 
+def _ws_bytes(workspace: torch.Tensor, device) -> int:
+    """Size in bytes of a caller's workspace tensor (any dtype), which must be contiguous device
+    memory on the tensors' device."""
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace.numel() * workspace.element_size()
+
+
 def workspace_for(S: int, B: int, H: int, dtype: torch.dtype, device) -> torch.Tensor:
     n = mccb_get_workspace_size(S, B, H, DTYPE_CODE[dtype])
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
@@ -230,7 +238,7 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
             workspace = workspace_for(S, B, H, dt, dev)
         rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
                            gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt],
-                           workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+                           workspace.data_ptr(), _ws_bytes(workspace, dev), st.cuda_stream)
         where = "mccb_backward"
     else:
         if workspace is None:
@@ -239,7 +247,8 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         rc = mccb_backward_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
                               gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, W, DTYPE_CODE[dt],
-                              strides, workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+                              strides, workspace.data_ptr(), _ws_bytes(workspace, dev),
+                              st.cuda_stream)
         where = "mccb_backward_ex"
     if rc != MCCB_OK:
         raise MccbError(rc, where)
@@ -284,8 +293,8 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
                                                    DTYPE_CODE[dt], strides)
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         rc = mccb_forward_ex(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H, W,
-                             DTYPE_CODE[dt], strides, workspace.data_ptr(), workspace.numel(),
-                             st.cuda_stream)
+                             DTYPE_CODE[dt], strides, workspace.data_ptr(),
+                             _ws_bytes(workspace, dev), st.cuda_stream)
         where = "mccb_forward_ex"
     if rc != MCCB_OK:
         raise MccbError(rc, where)
@@ -337,7 +346,7 @@ def varlen_backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     rc = mccb_varlen_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
                               None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
                               gradX.data_ptr(), gradWeight.data_ptr(), T, nseq, H, W,
-                              DTYPE_CODE[dt], workspace.data_ptr(), workspace.numel(),
+                              DTYPE_CODE[dt], workspace.data_ptr(), _ws_bytes(workspace, dev),
                               st.cuda_stream)
     if rc != MCCB_OK:
         raise MccbError(rc, "mccb_varlen_backward")
@@ -361,7 +370,7 @@ def varlen_forward(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tens
     rc = mccb_varlen_forward(x.data_ptr(), weight.data_ptr(),
                              None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
                              y.data_ptr(), T, nseq, H, W, DTYPE_CODE[dt], workspace.data_ptr(),
-                             workspace.numel(), st.cuda_stream)
+                             _ws_bytes(workspace, dev), st.cuda_stream)
     if rc != MCCB_OK:
         raise MccbError(rc, "mccb_varlen_forward")
     return y

@@ -371,3 +371,17 @@ def test_varlen_validation():
     assert rc == INVALID  # y overlapping x
     rc = mdc.mccb_varlen_forward(X, W, M, None, GX, 100, 3, 384, 3, BF16, WS, 1 << 40, None)
     assert rc == NULLPTR
+
+
+def test_binding_passes_workspace_bytes_of_any_dtype():
+    """The binding hands the library the workspace's size in bytes (numel * element size), and
+    refuses a non-contiguous workspace or one on another device."""
+    import torch
+
+    cpu = torch.device("cpu")
+    assert mdc._ws_bytes(torch.empty(10, dtype=torch.uint8), cpu) == 10
+    assert mdc._ws_bytes(torch.empty(10, dtype=torch.float32), cpu) == 40
+    with pytest.raises(ValueError):
+        mdc._ws_bytes(torch.empty(20, dtype=torch.uint8)[::2], cpu)
+    with pytest.raises(ValueError):
+        mdc._ws_bytes(torch.empty(10, dtype=torch.uint8), torch.device("meta"))
