@@ -10,24 +10,32 @@
 // Storage view: with C = B*H, the [S,B,H] tensors are an [S, C] row-major matrix; column
 // c = j*H + h never mixes with another column except that gradWeight sums the columns that share h.
 // So the whole op is a 3-tap stencil down the rows of that matrix plus a column-group reduction.
+// The same kernels take windows of W = 1..4 taps (weight [W,H], look-ahead W-1 rows), gradY and x
+// read in place with their own row and batch strides, and the packed variable-length layout
+// ([T,H] tokens with cumulative sequence lengths, the stencil cut at each sequence's end); the
+// forward y = mask * causal conv(x, w) is a separate one-pass kernel further down.
 //
-// Kernel 1 (fused): a lane owns kVec consecutive columns (one 4-byte load per row). A block is
-// kColGroups x kRing wavefronts (fewer column groups for the instantiations that need more
-// registers): kColGroups waves side by side cover kColGroups*64*kVec contiguous
-// columns, and kRing waves stacked on each column group take the rows of the block's strip round
-// robin, kTurnRows rows each per round, with a block barrier per round. So at any moment a block
-// reads one contiguous stretch of each of kRing*kTurnRows consecutive rows, and all its waves
-// advance together; each row of gradY, x and gradX crosses HBM once. A wave forms gradX for its
-// kTurnRows rows from the masked gradY rows i..i+kTurnRows+1 it holds in registers (the first two
-// are the previous wave's last look-ahead rows, loaded again and served from L2), and accumulates
-// its gradWeight terms in fp64 across all its rounds. Rounds are software-pipelined: a wave issues
-// the loads of its next turn before computing the current one, so HBM requests stay in flight
-// through the arithmetic and across the (fence-free) round barrier. The strip's mask bytes are staged in LDS
-// once. At the end the block sums the kRing waves of each column group in LDS in a fixed order and
-// writes one fp64 partial per (strip, tap, column) to the caller's workspace. Kernel 2 (reduce)
-// adds the partials of each (tap, channel) over strips and batches in a fixed order and rounds
-// once. No atomics anywhere: the result bits depend only on the inputs and the plan, and the plan
-// only on (S, B, H, dtype).
+// Kernel 1 (fused): the rows are cut into strips and the columns into blocks; a block walks its
+// strip down the rows, a wavefront holding one wave-wide load (64 lanes x V columns, a "column
+// group") of each row it handles. Two lane layouts, chosen from the shape alone:
+//   wide (windows of up to 3 taps, B*H a multiple of 32768): 8-byte lanes, 4 column groups per
+//     block placed 16 KiB apart in the row, one wave per group. Four wave-wide loads that far apart
+//     are served faster by the HBM than four adjacent ones.
+//   ring (everything else): 4-byte lanes, column groups of adjacent columns with 2 waves each,
+//     which take the strip's rows round robin.
+// Either way a wave takes kTurnRows rows per round, and the block's waves pass a barrier each
+// round, so the block's loads of a row reach the HBM together; each row of gradY, x and gradX
+// crosses HBM once. A wave forms gradX for its kTurnRows rows from the masked gradY rows
+// i..i+kTurnRows+W-2 it holds in registers (the first W-1 are the previous turn's look-ahead rows,
+// loaded again and served from L2), and accumulates its gradWeight terms in fp64 across all its
+// rounds. Rounds are software-pipelined: a wave issues the loads of its next turn before computing
+// the current one, so HBM requests stay in flight through the arithmetic and across the
+// (fence-free) round barrier. The strip's mask bytes are staged in LDS once. At the end each column
+// group writes one fp64 partial per (strip, tap, column) to the caller's workspace (the ring
+// layout first adds its two waves in LDS, in a fixed order). Kernel 2 (reduce) adds the partials
+// of each (tap, channel) over strips and batches in a fixed order and rounds once. No atomics
+// anywhere: the result bits depend only on the inputs and the plan, and the plan only on
+// (S, B, H, dtype, W).
 //
 // Precision: every product of two 16-bit values is exact in fp64 (and in fp32). gradX's three
 // products are summed in fp64 in the equation's order and the sum is rounded once to the dtype
@@ -44,18 +52,28 @@
 
 #include "mccb.h"
 
-// Tuning constants (compile-time; every value here gives the same results).
-#ifndef MCCB_VEC
-#define MCCB_VEC 2  // columns per lane: 2 -> 4-byte loads, 4 -> 8-byte loads
+// Tuning constants (compile-time; every value here gives the same results, except that the lane
+// layout of the fused kernel fixes the order in which gradWeight's fp64 partial sums are formed).
+// The wide layout of the fused kernel: MCCB_WIDE_VEC columns per lane, MCCB_WIDE_COL_GROUPS
+// column groups MCCB_GROUP_SPACING bytes apart with MCCB_WIDE_RING waves each. The ring layout
+// is fixed: 2 columns per lane, 4 adjacent column groups (2 where registers run short) of 2 waves.
+#ifndef MCCB_WIDE_VEC
+#define MCCB_WIDE_VEC 4  // columns per lane: 4 -> 8-byte loads
 #endif
-#ifndef MCCB_COL_GROUPS
-#define MCCB_COL_GROUPS 4  // waves side by side in a block (each 64 lanes x MCCB_VEC columns)
+#ifndef MCCB_WIDE_COL_GROUPS
+#define MCCB_WIDE_COL_GROUPS 4
 #endif
-#ifndef MCCB_RING
-#define MCCB_RING 2  // waves stacked along rows in a block, taking rows round robin
+#ifndef MCCB_WIDE_RING
+#define MCCB_WIDE_RING 1
+#endif
+#ifndef MCCB_WIDE_WAVES_PER_SIMD
+#define MCCB_WIDE_WAVES_PER_SIMD 2  // occupancy the wide layout is compiled for (caps its VGPRs)
+#endif
+#ifndef MCCB_GROUP_SPACING
+#define MCCB_GROUP_SPACING 16384  // bytes between the column groups of a wide block
 #endif
 #ifndef MCCB_TURN_ROWS
-#define MCCB_TURN_ROWS 8  // rows a wave handles per round (loads kept in flight together)
+#define MCCB_TURN_ROWS 8  // rows a wave handles per turn (loads kept in flight together)
 #endif
 #ifndef MCCB_NT_LOAD
 #define MCCB_NT_LOAD 1  // streaming (non-temporal) hint on gradY / x loads read once
@@ -63,17 +81,8 @@
 #ifndef MCCB_NT_STORE
 #define MCCB_NT_STORE 1  // streaming (non-temporal) hint on gradX stores
 #endif
-#ifndef MCCB_WAVES_PER_SIMD
-#define MCCB_WAVES_PER_SIMD 4  // occupancy the fused kernel is compiled for (caps its VGPRs)
-#endif
-#ifndef MCCB_NARROW_COL_GROUPS
-#define MCCB_NARROW_COL_GROUPS 2  // column groups of the variants compiled for one wave less
-#endif
 #ifndef MCCB_EXACT_GRADX
 #define MCCB_EXACT_GRADX 1  // 1: gradX correctly rounded from fp64; 0: fp64 -> fp32 -> dtype
-#endif
-#ifndef MCCB_ROUND_BARRIER
-#define MCCB_ROUND_BARRIER 1  // keep a block's waves on the same round
 #endif
 #ifndef MCCB_LDS_FLOOR
 #define MCCB_LDS_FLOOR 0  // dynamic LDS bytes the fused kernel reserves at least (caps blocks per CU)
@@ -108,23 +117,45 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;  // lanes per wavefront on CDNA
-constexpr int kVec = MCCB_VEC;  // columns per lane: one load of kVec 16-bit values
-constexpr int kWords = kVec / 2;
-constexpr int kColGroups = MCCB_COL_GROUPS;
-constexpr int kRing = MCCB_RING;
 constexpr int kTurnRows = MCCB_TURN_ROWS;
-constexpr int kBlockWaves = kColGroups * kRing;
-constexpr int kGroupCols = kWave * kVec;             // columns of one column group
-constexpr int kBlockCols = kColGroups * kGroupCols;  // columns of one block
-constexpr int kRoundRows = kRing * kTurnRows;        // rows a block advances per round
-constexpr int kMaxBatchesPerBlock = 3;  // 512 or fewer columns span at most 3 batches if H >= 384
+constexpr int kPlanRound = 16;  // strips are a whole number of this many rows (any layout's round)
+constexpr int kPlanMaxStripRows = 784;  // longest strip the plan makes for S >= 768 (sizing only)
 constexpr int kReduceWaves = 16;        // wavefronts per reduce block
 constexpr int kReduceCols = kWave * 2;  // channels per reduce block (2 fp64 per lane)
-static_assert(kVec == 2 || kVec == 4, "lane vector must be 4 or 8 bytes");
-static_assert(kBlockCols <= 512, "mask staging assumes a block spans at most 3 batches");
-static_assert(kBlockWaves * kWave <= 1024, "block too large");
 
-typedef uint32_t vec_t __attribute__((ext_vector_type(kWords)));
+// Lane vector of V 16-bit values (V/2 words): one load per row.
+template <int V>
+struct Vec {
+    typedef uint32_t t __attribute__((ext_vector_type(V / 2)));
+};
+
+// Lane layouts of the fused kernel (all give each column's gradX bit for bit; gradWeight's fp64
+// partials are summed in the layout's order, and the layout is a function of the shape only):
+//   WIDE (windows of up to 3 taps, rows a whole number of super-chunks): 8-byte lanes, a block is
+//        4 column groups spaced MCCB_GROUP_SPACING bytes apart, one wave per group;
+//   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
+//        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
+//        4-tap windows).
+template <int W, bool STRIDED, bool WIDE>
+struct FusedCfg {
+    static constexpr bool tight = (STRIDED && W >= 3) || W > 3;
+    static constexpr int V = WIDE ? MCCB_WIDE_VEC : 2;  // columns per lane
+    static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS : (tight ? 2 : 4);
+    static constexpr int RG = WIDE ? MCCB_WIDE_RING : 2;  // waves per column group
+    static constexpr int WPS = WIDE ? MCCB_WIDE_WAVES_PER_SIMD : (tight ? 3 : 4);
+    static constexpr int GC = kWave * V;       // columns of one column group
+    static constexpr int BW = CG * RG;         // waves per block
+    static constexpr int RR = RG * kTurnRows;  // rows a block advances per round
+    // column groups spaced this many lane vectors apart (0: adjacent)
+    static constexpr int64_t DLV = WIDE ? (int64_t)MCCB_GROUP_SPACING / (V * 2) : 0;
+    static_assert(!WIDE || W <= 3, "the wide layout holds at most 3 taps of fp64 state");
+    static_assert(V == 2 || V == 4, "lane vector must be 4 or 8 bytes");
+    static_assert(GC < 384, "a column group spans at most 2 batches (H >= 384)");
+    static_assert(CG <= 4, "the staged mask holds two batches for each of at most 4 groups");
+    static_assert(kPlanRound % RR == 0, "strips must be whole rounds");
+    static_assert(BW * kWave <= 1024, "block too large");
+    static_assert(DLV % kWave == 0, "group spacing must be a whole number of wave-wide loads");
+};
 
 constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
@@ -133,6 +164,13 @@ constexpr int64_t kStripRows = MCCB_STRIP_ROWS;
 constexpr int64_t kMinBlocks = MCCB_MIN_BLOCKS;
 constexpr int64_t kMinStripRows = MCCB_MIN_STRIP_ROWS;
 constexpr int64_t kMaxMaskLds = 48 * 1024;  // bytes of LDS for the staged mask, at most
+// The strip rule counts column blocks of this many columns (its tuning predates the wide layout;
+// the strips, not the launch width, fix gradWeight's summation order).
+constexpr int64_t kPlanBlockCols = 512;
+// Columns of the widest column group (one wave-wide load) of the fused kernel.
+constexpr int64_t kMaxGroupCols = (int64_t)kWave * (MCCB_WIDE_VEC > 2 ? MCCB_WIDE_VEC : 2);
+// Staged mask batches per block: two per column group (a group's columns span at most two).
+constexpr int kMaxStagedBatches = 2 * (MCCB_WIDE_COL_GROUPS > 4 ? MCCB_WIDE_COL_GROUPS : 4);
 
 // ---------------------------------------------------------------------------------------------
 // 16-bit formats
@@ -176,21 +214,26 @@ __device__ static inline float round_to_odd_f32(double d) {
     return __uint_as_float(back != d ? (toward_zero | 1u) : b);
 }
 
-template <int DT>
-__device__ static inline void unpack_vec(const vec_t q, float (&f)[kVec]) {
+template <int DT, int V>
+__device__ static inline void unpack_vec(const typename Vec<V>::t q, float (&f)[V]) {
 #pragma unroll
-    for (int p = 0; p < kWords; ++p) Fmt<DT>::unpack(q[p], f[2 * p], f[2 * p + 1]);
+    for (int p = 0; p < V / 2; ++p) Fmt<DT>::unpack(q[p], f[2 * p], f[2 * p + 1]);
 }
 
-__device__ static inline vec_t load_vec(const vec_t *p) {
+template <typename T>
+__device__ static inline T load_vec(const T *p) {
 #if MCCB_NT_LOAD
     return __builtin_nontemporal_load(p);
 #else
     return *p;
 #endif
 }
-__device__ static inline vec_t load_vec_cached(const vec_t *p) { return *p; }
-__device__ static inline void store_vec(vec_t *p, vec_t v) {
+template <typename T>
+__device__ static inline T load_vec_cached(const T *p) {
+    return *p;
+}
+template <typename T>
+__device__ static inline void store_vec(T *p, T v) {
 #if MCCB_NT_STORE
     __builtin_nontemporal_store(v, p);
 #else
@@ -198,19 +241,20 @@ __device__ static inline void store_vec(vec_t *p, vec_t v) {
 #endif
 }
 
-// gradX for one lane's kVec columns at row i from the masked gradY rows i .. i+W-1 (fp64, d[k] =
+// gradX for one lane's V columns at row i from the masked gradY rows i .. i+W-1 (fp64, d[k] =
 // gYm[i+k]), and the gradWeight terms of row i: a[k] += gYm[i+W-1-k] * x[i]. Returns the packed
 // gradX row. LIMITED (packed variable-length layout): only d[k] with k < lim belong to row i's
 // sequence; the rest count as zero.
-template <int DT, int W, bool LIMITED = false>
-__device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec_t x_row,
-                                           const double (&wt)[W][kVec], double (&a)[W][kVec],
-                                           int lim = W) {
-    float xf[kVec];
-    unpack_vec<DT>(x_row, xf);
-    float out[kVec];
+template <int DT, int W, int V, bool LIMITED = false>
+__device__ static inline typename Vec<V>::t stencil_row(const double (&d)[W][V],
+                                                       const typename Vec<V>::t x_row,
+                                                       const double (&wt)[W][V],
+                                                       double (&a)[W][V], int lim = W) {
+    float xf[V];
+    unpack_vec<DT, V>(x_row, xf);
+    float out[V];
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) {
+    for (int e = 0; e < V; ++e) {
         // gradX[i] = sum_k gYm[i+k] * w[W-1-k], in k order (each product exact in fp64)
         double s = d[0][e] * wt[W - 1][e];
 #pragma unroll
@@ -228,111 +272,139 @@ __device__ static inline vec_t stencil_row(const double (&d)[W][kVec], const vec
             a[k][e] = __builtin_fma((!LIMITED || W - 1 - k < lim) ? d[W - 1 - k][e] : 0.0, xd,
                                     a[k][e]);
     }
-    vec_t r;
+    typename Vec<V>::t r;
 #pragma unroll
-    for (int p = 0; p < kWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
+    for (int p = 0; p < V / 2; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
     return r;
 }
 
-template <int DT>
-__device__ static inline void widen(const vec_t q, double (&d)[kVec]) {
-    float f[kVec];
-    unpack_vec<DT>(q, f);
+template <int DT, int V>
+__device__ static inline void widen(const typename Vec<V>::t q, double (&d)[V]) {
+    float f[V];
+    unpack_vec<DT, V>(q, f);
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) d[e] = (double)f[e];
+    for (int e = 0; e < V; ++e) d[e] = (double)f[e];
 }
 
 // ---------------------------------------------------------------------------------------------
 // Kernel 1: mask + gradX + gradWeight partials in one HBM pass, for a window of W taps (the
 // look-ahead is W-1 rows).
-// grid.x = n_col_blocks * n_strips (column block fastest), block = CG * kRing waves with CG =
-// fused_col_groups(STRIDED, W) column groups.
-// Dynamic LDS (masked launches only): kMaxBatchesPerBlock * (rows_per_strip + W - 1) mask bytes.
+// grid.x = n_col_blocks * n_strips (column block fastest), block = CG * RG waves (FusedCfg<W>).
+// Dynamic LDS (masked launches): CG * 2 * (rows_per_strip + W - 1) mask bytes, then (VARLEN) the
+// strip's rows_per_strip + W - 1 `ahead` bytes.
 // Workspace: fp64 partials [n_strips][W][C].
+//
+// Columns of a block: a column group is one wave-wide load of each row (64 lanes x V columns).
+// Column blocks below `n_sp_blocks` place their CG groups DLV lane vectors apart (a super-chunk of
+// CG*DLV lane vectors is covered by DLV/64 such blocks); the rest of the row is cut into blocks of
+// CG adjacent groups. Every lane vector of a row belongs to exactly one lane of one block.
 // ---------------------------------------------------------------------------------------------
 // Input strides (in elements; channels contiguous, so only the row and batch strides vary): a
 // contiguous [S,B,H] tensor has row stride B*H and batch stride H. With STRIDED false the kernel
 // assumes that layout for gradY and x; with STRIDED true it takes each tensor's own strides. Either
-// way a load address is a wave-uniform 64-bit base (row, and for STRIDED the block's first batch)
-// plus a 32-bit lane offset; the host reads an input in place only when that offset fits (a block
-// spans at most three batches). The mask is always addressed through its strides (batch, row),
-// which cost nothing in the once-per-strip staging loop.
+// way a load address is a wave-uniform 64-bit base (row, and for STRIDED the wave's first batch)
+// plus a 32-bit lane offset; a wave's columns span at most two batches, and the host reads an
+// input in place only when the lane offset fits. The mask is always addressed through its strides
+// (batch, row), which cost nothing in the once-per-strip staging loop.
 struct InStrides {
     int64_t gy_row, gy_batch, x_row, x_batch, m_batch, m_row;
 };
 
-// Register budget: the strided variant keeps a second lane offset and row stride, and a wider
-// window keeps more fp64 state; such variants are compiled for one wavefront less per SIMD so that
-// they do not spill, and their blocks are narrower (fewer column groups) so that a CU still holds
-// two or more of them: with one wavefront less per SIMD a CU has room for only one full block.
-// The block shape does not enter the arithmetic: each column's partial is the same sum of the
-// same ring waves' turns whatever the number of column groups beside it.
-constexpr bool fused_narrow(bool strided, int w) { return (strided && w >= 3) || w > 3; }
-constexpr int fused_waves_per_simd(bool strided, int w) {
-    return fused_narrow(strided, w) ? MCCB_WAVES_PER_SIMD - 1 : MCCB_WAVES_PER_SIMD;
+// First lane vector (lane 0) of column group g of column block cb.
+template <int CG>
+__device__ static inline int64_t group_first_vec(int64_t cb, int g, int64_t n_sp_blocks,
+                                                 int64_t dlv) {
+    if (cb < n_sp_blocks) {
+        const int64_t per = dlv / kWave;  // blocks per super-chunk
+        const int64_t sup = cb / per, k = cb - sup * per;
+        return sup * CG * dlv + g * dlv + k * kWave;
+    }
+    return n_sp_blocks * CG * kWave + ((cb - n_sp_blocks) * CG + g) * kWave;
 }
-constexpr int fused_col_groups(bool strided, int w) {
-    return fused_narrow(strided, w) ? MCCB_NARROW_COL_GROUPS : kColGroups;
-}
-static_assert(MCCB_NARROW_COL_GROUPS >= 1 && MCCB_NARROW_COL_GROUPS <= kColGroups,
-              "narrow blocks must not be wider than the full ones");
 
 // VARLEN (packed variable-length layout, B = 1): `ahead[i]` holds the number of rows i, i+1, ...
-// that belong to row i's sequence (at least 1); the stencil of row i uses only those. The bytes of
-// the strip are staged in LDS after the mask's `lim_lds` bytes.
-template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN = false>
-__global__ void __launch_bounds__(fused_col_groups(STRIDED, W) * kRing * kWave)
-    __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(STRIDED, W))))
-    mccb_fused_bwd(const vec_t *__restrict__ gy, const vec_t *__restrict__ x,
-                   const vec_t *__restrict__ w, const uint8_t *__restrict__ mask,
-                   vec_t *__restrict__ gx, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
-                   int64_t rows_per_strip, int64_t n_col_blocks, InStrides st,
-                   const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
+// that belong to row i's sequence (at least 1); the stencil of row i uses only those.
+template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN, bool WIDE>
+__global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
+    __attribute__((amdgpu_waves_per_eu((FusedCfg<W, STRIDED, WIDE>::WPS))))
+    mccb_fused_bwd(const void *__restrict__ gy_, const void *__restrict__ x_,
+                   const void *__restrict__ w_, const uint8_t *__restrict__ mask,
+                   void *__restrict__ gx_, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
+                   int64_t rows_per_strip, int64_t n_col_blocks, int64_t n_sp_blocks,
+                   InStrides st, const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
+    typedef FusedCfg<W, STRIDED, WIDE> Cfg;
+    constexpr int V = Cfg::V, CG = Cfg::CG, RG = Cfg::RG, TR = kTurnRows, RR = Cfg::RR;
+    typedef typename Vec<V>::t vec_t;
     constexpr int L = W - 1;  // look-ahead rows
-    constexpr int CG = fused_col_groups(STRIDED, W);  // column groups side by side
-    constexpr int BW = CG * kRing;                     // waves per block
-    constexpr int BC = CG * kGroupCols;                // columns per block
     extern __shared__ uint8_t smask[];
-    __shared__ f64x2 red[BW][kWave * kVec / 2];
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane of a wave; saying so keeps everything derived from
     // it (row ranges, row addresses) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int ring = wave / CG;  // position along rows
+    const int ring = wave / CG;   // position along rows
     const int group = wave % CG;  // column group
     const int64_t C = B * H;
-    const int64_t CV = C / kVec;  // lane vectors per row
+    const int64_t CV = C / V;  // lane vectors per row
     const int64_t col_block = blockIdx.x % n_col_blocks;
     const int64_t strip = blockIdx.x / n_col_blocks;
     const int64_t rs0 = strip * rows_per_strip;
     const int64_t rs1 = (rs0 + rows_per_strip < S) ? rs0 + rows_per_strip : S;
 
     // Lanes past the last column load a valid column (the last one) and store nothing.
-    const int64_t v_raw = (col_block * CG + group) * kWave + lane;
+    const int64_t v0 = group_first_vec<CG>(col_block, group, n_sp_blocks, Cfg::DLV);
+    const int64_t v_raw = v0 + lane;
     const bool active = v_raw < CV;
     const int64_t v = active ? v_raw : CV - 1;
-    const int64_t c = v * kVec;
+    const int64_t c = v * V;
     const int64_t j = c / H;
     const int64_t h = c - j * H;
+    const int64_t jg = ((v0 < CV ? v0 : CV - 1) * V) / H;  // the wave's first batch
 
+    const int span = (int)(rows_per_strip + L);  // staged rows of the strip
     int moff = 0;  // offset of this lane's batch in the staged mask
     if constexpr (HAS_MASK) {
-        const int64_t c_first = col_block * BC;
-        const int64_t c_last = (c_first + BC < C ? c_first + BC : C) - 1;
-        const int64_t j_first = c_first / H;
-        const int nj = (int)(c_last / H - j_first + 1);
-        const int span = (int)(rows_per_strip + L);
-        for (int t = threadIdx.x; t < nj * span; t += blockDim.x) {
-            const int jj = t / span;
-            const int64_t row = rs0 + (t - jj * span);
-            smask[t] = (row < S) ? mask[(j_first + jj) * st.m_batch + row * st.m_row] : (uint8_t)0;
+        // Each column group stages the bytes of its (at most two) batches: [CG][2][span]; the
+        // second slot only when the group's columns reach into the next batch. A thread issues
+        // the loads of a batch of its bytes before writing any of them to LDS, so that it waits
+        // once per batch instead of once per byte.
+        int64_t jf[CG];
+        bool two[CG];
+#pragma unroll
+        for (int gg = 0; gg < CG; ++gg) {
+            const int64_t vg = group_first_vec<CG>(col_block, gg, n_sp_blocks, Cfg::DLV);
+            const int64_t va = vg < CV ? vg : CV - 1, vb = vg + kWave - 1 < CV ? vg + kWave - 1 : CV - 1;
+            jf[gg] = (va * V) / H;
+            two[gg] = (vb * V + V - 1) / H != jf[gg];
         }
-        moff = (int)(j - j_first) * span;
+        auto mask_byte = [&](int t) -> uint8_t {
+            const int slot = t / span;  // group * 2 + batch within the group
+            const int gg = slot >> 1;
+            if ((slot & 1) && !two[gg]) return 0;
+            const int64_t jj = jf[gg] + (slot & 1);
+            const int64_t row = rs0 + (t - slot * span);
+            return (row < S) ? mask[jj * st.m_batch + row * st.m_row] : (uint8_t)0;
+        };
+        constexpr int kThreads = Cfg::BW * kWave;
+        constexpr int kStage = (2 * CG * (kPlanMaxStripRows + 3) + kThreads - 1) / kThreads;
+        const int n = CG * 2 * span;
+        for (int base = 0; base < n; base += kStage * kThreads) {
+            uint8_t vals[kStage];
+#pragma unroll
+            for (int q = 0; q < kStage; ++q) {
+                const int t = base + q * kThreads + (int)threadIdx.x;
+                vals[q] = (t < n) ? mask_byte(t) : (uint8_t)0;
+            }
+#pragma unroll
+            for (int q = 0; q < kStage; ++q) {
+                const int t = base + q * kThreads + (int)threadIdx.x;
+                if (t < n) smask[t] = vals[q];
+            }
+        }
+        moff = (group * 2 + (int)(j - jg)) * span;
         if constexpr (!VARLEN) __syncthreads();
     }
     if constexpr (VARLEN) {
-        const int span = (int)(rows_per_strip + L);
         for (int t = threadIdx.x; t < span; t += blockDim.x) {
             const int64_t row = rs0 + t;
             smask[lim_lds + t] = (row < S) ? ahead[row] : (uint8_t)1;
@@ -345,24 +417,25 @@ __global__ void __launch_bounds__(fused_col_groups(STRIDED, W) * kRing * kWave)
         return W;
     };
 
-    double wt[W][kVec];
+    const vec_t *w = reinterpret_cast<const vec_t *>(w_);
+    double wt[W][V];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        float t[kVec];
-        unpack_vec<DT>(w[(k * H + h) / kVec], t);
+        float t[V];
+        unpack_vec<DT, V>(w[(k * H + h) / V], t);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) wt[k][e] = (double)t[e];
+        for (int e = 0; e < V; ++e) wt[k][e] = (double)t[e];
     }
 
-    double a[W][kVec];
+    double a[W][V];
 #pragma unroll
     for (int k = 0; k < W; ++k)
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) a[k][e] = 0.0;
+        for (int e = 0; e < V; ++e) a[k][e] = 0.0;
 
     vec_t zero;
 #pragma unroll
-    for (int p = 0; p < kWords; ++p) zero[p] = 0u;
+    for (int p = 0; p < V / 2; ++p) zero[p] = 0u;
     // Whether the mask keeps gradY row `row` of this lane's batch (rows < S only).
     auto keep = [&](int64_t row) -> bool {
         if constexpr (HAS_MASK) return smask[moff + (int)(row - rs0)] != 0;
@@ -372,15 +445,14 @@ __global__ void __launch_bounds__(fused_col_groups(STRIDED, W) * kRing * kWave)
     // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
     // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
     const int64_t row_bytes = C * 2;
-    const uint32_t lane_off = (uint32_t)(v * (kVec * 2));
-    // STRIDED: the block's first batch goes into the uniform base, the lane keeps the rest
-    const int64_t jb = (col_block * BC) / H;
-    const char *gy_base = reinterpret_cast<const char *>(gy) + (STRIDED ? jb * st.gy_batch * 2 : 0);
-    const char *x_base = reinterpret_cast<const char *>(x) + (STRIDED ? jb * st.x_batch * 2 : 0);
+    const uint32_t lane_off = (uint32_t)(v * (V * 2));
+    // STRIDED: the wave's first batch goes into the uniform base, the lane keeps the rest
+    const char *gy_base = reinterpret_cast<const char *>(gy_) + (STRIDED ? jg * st.gy_batch * 2 : 0);
+    const char *x_base = reinterpret_cast<const char *>(x_) + (STRIDED ? jg * st.x_batch * 2 : 0);
     const int64_t gy_rb = STRIDED ? st.gy_row * 2 : row_bytes;
     const int64_t x_rb = STRIDED ? st.x_row * 2 : row_bytes;
-    const uint32_t gy_lane = STRIDED ? (uint32_t)(((j - jb) * st.gy_batch + h) * 2) : lane_off;
-    const uint32_t x_lane = STRIDED ? (uint32_t)(((j - jb) * st.x_batch + h) * 2) : lane_off;
+    const uint32_t gy_lane = STRIDED ? (uint32_t)(((j - jg) * st.gy_batch + h) * 2) : lane_off;
+    const uint32_t x_lane = STRIDED ? (uint32_t)(((j - jg) * st.x_batch + h) * 2) : lane_off;
     auto at_gy = [&](int64_t row) -> const vec_t * {
         return reinterpret_cast<const vec_t *>(gy_base + row * gy_rb + gy_lane);
     };
@@ -388,119 +460,131 @@ __global__ void __launch_bounds__(fused_col_groups(STRIDED, W) * kRing * kWave)
         return reinterpret_cast<const vec_t *>(x_base + row * x_rb + x_lane);
     };
     auto out_at = [&](int64_t row) -> vec_t * {
-        return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx) + row * row_bytes + lane_off);
+        return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx_) + row * row_bytes + lane_off);
     };
 
-    // A turn is "whole" when this wave's kTurnRows rows and their look-ahead rows all exist.
+    // A turn is "whole" when this wave's TR rows and their look-ahead rows all exist.
     auto whole = [&](int64_t r0) {
-        const int64_t i0 = r0 + ring * kTurnRows;
-        return i0 + kTurnRows <= rs1 && i0 + kTurnRows + L <= S;
+        const int64_t i0 = r0 + ring * TR;
+        return i0 + TR <= rs1 && i0 + TR + L <= S;
     };
-    // Issue the loads of a whole turn: gradY rows i0 .. i0+kTurnRows+L-1 and x rows i0 ..
-    // i0+kTurnRows-1. The first L gradY rows were the previous wave's last look-ahead rows, and this
-    // wave's last L are the next wave's first: cached loads, so those come from L2; the rest stream.
-    auto issue = [&](int64_t r0, vec_t (&qy)[kTurnRows + L], vec_t (&qx)[kTurnRows]) {
-        const int64_t i0 = r0 + ring * kTurnRows;
+    // Issue the loads of a whole turn: gradY rows i0 .. i0+TR+L-1 and x rows i0 .. i0+TR-1. The
+    // first L gradY rows were the previous turn's last look-ahead rows (this wave's own with one
+    // wave per group, the other ring wave's otherwise), and this turn's last L are the next turn's
+    // first: cached loads, so those come from L2; the rest stream.
+    auto issue = [&](int64_t r0, vec_t (&qy)[TR + L], vec_t (&qx)[TR]) {
+        const int64_t i0 = r0 + ring * TR;
 #pragma unroll
         for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(at_gy(i0 + k));
 #pragma unroll
-        for (int u = 0; u < kTurnRows; ++u) {
-            qy[u + L] = (u + L >= kTurnRows) ? load_vec_cached(at_gy(i0 + L + u))
-                                             : load_vec(at_gy(i0 + L + u));
+        for (int u = 0; u < TR; ++u) {
+            qy[u + L] = (u + L >= TR) ? load_vec_cached(at_gy(i0 + L + u))
+                                      : load_vec(at_gy(i0 + L + u));
             qx[u] = load_vec(at_x(i0 + u));
         }
     };
-    auto compute = [&](int64_t r0, const vec_t (&qy)[kTurnRows + L], const vec_t (&qx)[kTurnRows]) {
-        const int64_t i0 = r0 + ring * kTurnRows;
-        double d[W][kVec];
+    auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
+        const int64_t i0 = r0 + ring * TR;
+        double d[W][V];
 #pragma unroll
-        for (int k = 0; k < L; ++k) widen<DT>(keep(i0 + k) ? qy[k] : zero, d[k]);
+        for (int k = 0; k < L; ++k) widen<DT, V>(keep(i0 + k) ? qy[k] : zero, d[k]);
 #pragma unroll
-        for (int u = 0; u < kTurnRows; ++u) {
-            widen<DT>(keep(i0 + L + u) ? qy[u + L] : zero, d[L]);
+        for (int u = 0; u < TR; ++u) {
+            widen<DT, V>(keep(i0 + L + u) ? qy[u + L] : zero, d[L]);
             vec_t r;
             if constexpr (VARLEN) {
                 // a uniform branch: only the last W-1 rows of a sequence take the limited form
                 const int lim = lim_of(i0 + u);
                 if (lim >= W)
-                    r = stencil_row<DT, W>(d, qx[u], wt, a);
+                    r = stencil_row<DT, W, V>(d, qx[u], wt, a);
                 else
-                    r = stencil_row<DT, W, true>(d, qx[u], wt, a, lim);
+                    r = stencil_row<DT, W, V, true>(d, qx[u], wt, a, lim);
             } else {
-                r = stencil_row<DT, W>(d, qx[u], wt, a);
+                r = stencil_row<DT, W, V>(d, qx[u], wt, a);
             }
             if (active) store_vec(out_at(i0 + u), r);
 #pragma unroll
             for (int k = 0; k < L; ++k)
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) d[k][e] = d[k + 1][e];
+                for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
         }
     };
     // Partial turn at the end of the strip or of the tensor: one row at a time, gradY rows past S
     // read as zero.
     auto partial = [&](int64_t r0) {
-        const int64_t i0 = r0 + ring * kTurnRows;
+        const int64_t i0 = r0 + ring * TR;
         if (i0 >= rs1) return;
-        const int64_t i1 = (i0 + kTurnRows < rs1) ? i0 + kTurnRows : rs1;
-        double d[W][kVec];
+        const int64_t i1 = (i0 + TR < rs1) ? i0 + TR : rs1;
+        double d[W][V];
 #pragma unroll
         for (int k = 0; k < L; ++k)
-            widen<DT>((i0 + k < S && keep(i0 + k)) ? load_vec_cached(at_gy(i0 + k)) : zero, d[k]);
+            widen<DT, V>((i0 + k < S && keep(i0 + k)) ? load_vec_cached(at_gy(i0 + k)) : zero, d[k]);
         for (int64_t i = i0; i < i1; ++i) {
-            widen<DT>((i + L < S && keep(i + L)) ? load_vec_cached(at_gy(i + L)) : zero, d[L]);
-            const vec_t r = VARLEN ? stencil_row<DT, W, true>(d, load_vec(at_x(i)), wt, a, lim_of(i))
-                                   : stencil_row<DT, W>(d, load_vec(at_x(i)), wt, a);
+            widen<DT, V>((i + L < S && keep(i + L)) ? load_vec_cached(at_gy(i + L)) : zero, d[L]);
+            const vec_t r = VARLEN ? stencil_row<DT, W, V, true>(d, load_vec(at_x(i)), wt, a, lim_of(i))
+                                   : stencil_row<DT, W, V>(d, load_vec(at_x(i)), wt, a);
             if (active) store_vec(out_at(i), r);
 #pragma unroll
             for (int k = 0; k < L; ++k)
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) d[k][e] = d[k + 1][e];
+                for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
         }
     };
     // One round: prefetch the next round's whole turn into `nxt`, then compute this round from
     // `cur` (loaded one round earlier) while those loads are in flight.
-    auto round = [&](int64_t r0, const vec_t (&cy)[kTurnRows + L], const vec_t (&cx)[kTurnRows],
-                     vec_t (&ny)[kTurnRows + L], vec_t (&nx)[kTurnRows]) {
-        const int64_t rn = r0 + kRoundRows;
+    auto round = [&](int64_t r0, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR],
+                     vec_t (&ny)[TR + L], vec_t (&nx)[TR]) {
+        const int64_t rn = r0 + RR;
         if (rn < rs1 && whole(rn)) issue(rn, ny, nx);
         if (whole(r0))
             compute(r0, cy, cx);
         else
             partial(r0);
-#if MCCB_ROUND_BARRIER
-        // Keep the block's waves on the same round. A bare barrier, without a memory fence, so
-        // the prefetched loads stay in flight across it.
+        // Keep the block's waves on the same round: ring waves share look-ahead rows through L2,
+        // and the column groups' loads of a row reach the HBM together. A bare barrier, without a
+        // memory fence, so the prefetched loads stay in flight across it.
         __builtin_amdgcn_s_barrier();
-#endif
     };
 
-    vec_t ay[kTurnRows + L], ax[kTurnRows], by[kTurnRows + L], bx[kTurnRows];
+    vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
     if (whole(rs0)) issue(rs0, ay, ax);
     // Unrolled by two so that the two register buffers swap roles without copies.
-    for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * kRoundRows) {
+    for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
         round(r0, ay, ax, by, bx);
-        if (r0 + kRoundRows >= rs1) break;
-        round(r0 + kRoundRows, by, bx, ay, ax);
+        if (r0 + RR >= rs1) break;
+        round(r0 + RR, by, bx, ay, ax);
     }
 
-    // gradWeight partials of the strip: for each column group add its kRing waves in a fixed
-    // order (ring position 0 first).
-    const int64_t col0 = col_block * BC;
+    // gradWeight partials of the strip, one fp64 value per (tap, column).
+    if constexpr (RG == 1) {
+        // one wave per column group: the lane's own sums are the partials
+        if (active) {
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-        __syncthreads();
+            for (int k = 0; k < W; ++k)
 #pragma unroll
-        for (int p = 0; p < kVec / 2; ++p)
-            red[wave][lane * (kVec / 2) + p] = f64x2{a[k][2 * p], a[k][2 * p + 1]};
-        __syncthreads();
-        const double *flat = reinterpret_cast<const double *>(&red[0][0]);
-        for (int t = threadIdx.x; t < BC; t += blockDim.x) {
-            const int g = t / kGroupCols, within = t - g * kGroupCols;
-            double s = flat[g * kGroupCols + within];
+                for (int p = 0; p < V / 2; ++p)
+                    *reinterpret_cast<f64x2 *>(ws + (strip * W + k) * C + c + 2 * p) =
+                        f64x2{a[k][2 * p], a[k][2 * p + 1]};
+        }
+    } else {
+        // add the RG waves of each column group in a fixed order (ring position 0 first)
+        __shared__ f64x2 red[Cfg::BW][kWave * V / 2];
 #pragma unroll
-            for (int q = 1; q < kRing; ++q) s += flat[(q * CG + g) * kGroupCols + within];
-            const int64_t col = col0 + t;
-            if (col < C) ws[(strip * W + k) * C + col] = s;
+        for (int k = 0; k < W; ++k) {
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < V / 2; ++p)
+                red[wave][lane * (V / 2) + p] = f64x2{a[k][2 * p], a[k][2 * p + 1]};
+            __syncthreads();
+            if (ring == 0 && active) {
+#pragma unroll
+                for (int p = 0; p < V / 2; ++p) {
+                    f64x2 sum = red[group][lane * (V / 2) + p];
+#pragma unroll
+                    for (int q = 1; q < RG; ++q) sum += red[q * CG + group][lane * (V / 2) + p];
+                    *reinterpret_cast<f64x2 *>(ws + (strip * W + k) * C + c + 2 * p) = sum;
+                }
+            }
         }
     }
 }
@@ -806,14 +890,14 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype, int W = 3) {
     p.C = B * H;
     p.dtype = dtype;
     p.W = W;
-    p.n_col_blocks = (p.C + kBlockCols - 1) / kBlockCols;
+    p.n_col_blocks = (p.C + kPlanBlockCols - 1) / kPlanBlockCols;
     // Split the rows into strips of about kStripRows rows, more if the grid would have fewer than
     // kMinBlocks blocks (too few to keep every CU busy), but none shorter than kMinStripRows rows;
     // strips are a whole number of rounds long. Short-lived blocks keep the rows in flight across
     // the GPU close together, which the HBM serves faster than long independent column walks; each
     // strip costs 8*W bytes per column of partials written and read back, against 6 bytes per
     // element streamed.
-    const int64_t max_strips = (S + kRoundRows - 1) / kRoundRows;
+    const int64_t max_strips = (S + kPlanRound - 1) / kPlanRound;
     int64_t strips = (S + kStripRows - 1) / kStripRows;
     const int64_t fill = (kMinBlocks + p.n_col_blocks - 1) / p.n_col_blocks;
     if (strips < fill) strips = fill;
@@ -823,8 +907,8 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype, int W = 3) {
     if (strips < 1) strips = 1;
     for (;;) {
         const int64_t rows = (S + strips - 1) / strips;
-        p.rows_per_strip = (rows + kRoundRows - 1) / kRoundRows * kRoundRows;
-        p.mask_lds = (size_t)kMaxBatchesPerBlock * (size_t)(p.rows_per_strip + W - 1);
+        p.rows_per_strip = (rows + kPlanRound - 1) / kPlanRound * kPlanRound;
+        p.mask_lds = (size_t)kMaxStagedBatches * (size_t)(p.rows_per_strip + W - 1);
         if (p.mask_lds <= (size_t)kMaxMaskLds || strips >= max_strips) break;
         ++strips;  // keep the staged mask within its LDS budget
     }
@@ -848,11 +932,92 @@ struct Profile {
     std::vector<hipEvent_t> ev;  // 3 per call: before kernel 1, between, after kernel 2
 } g_prof;
 
-// Column blocks of a fused-kernel variant with `cg` column groups. The strips (and with them the
-// gradWeight summation order) come from the plan alone; only the launch's width varies.
-int64_t col_blocks(int64_t C, int cg) {
-    const int64_t cols = (int64_t)cg * kGroupCols;
-    return (C + cols - 1) / cols;
+// Column blocks of the fused kernel for a W-tap window: `ncb` in all, of which the first `n_sp`
+// place their column groups DLV lane vectors apart (whole super-chunks of CG*DLV lane vectors);
+// the rest of the row is cut into blocks of adjacent groups. The strips (and with them the
+// gradWeight summation order) come from the plan alone.
+struct FusedGrid {
+    int64_t ncb, n_sp;
+};
+template <int W, bool STRIDED, bool WIDE>
+FusedGrid fused_grid(int64_t C) {
+    typedef FusedCfg<W, STRIDED, WIDE> Cfg;
+    const int64_t CV = C / Cfg::V;
+    FusedGrid g;
+    g.n_sp = Cfg::DLV > 0 ? CV / (Cfg::CG * Cfg::DLV) * (Cfg::DLV / kWave) : 0;
+    const int64_t rest = CV - g.n_sp * Cfg::CG * kWave;
+    g.ncb = g.n_sp + (rest + Cfg::CG * kWave - 1) / (Cfg::CG * kWave);
+    return g;
+}
+
+// The wide layout is used for windows of up to 3 taps (padded layouts) when a row of B*H columns
+// is a whole number of its super-chunks (CG groups x the group spacing); elsewhere the ring layout.
+// A function of the shape only, so gradWeight's summation order is too.
+bool fused_wide(int64_t C, int64_t W) {
+    typedef FusedCfg<3, false, true> Cfg;
+    return W <= 3 && Cfg::DLV > 0 && (C / Cfg::V) % (Cfg::CG * Cfg::DLV) == 0;
+}
+
+// Columns per lane of the fused kernel that a call runs (its loads' size and alignment).
+int fused_vec(int64_t C, int64_t W) {
+    return fused_wide(C, W) ? FusedCfg<3, false, true>::V : FusedCfg<3, false, false>::V;
+}
+
+template <int DT, bool M, bool T, int TAPS, bool VL, bool WD>
+hipError_t launch_fused(const Plan &p, const void *gy, const void *x, const void *w,
+                        const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
+                        const InStrides &is, const uint8_t *ahead, int lim_lds) {
+    const FusedGrid fg = fused_grid<TAPS, T, WD>(p.C);
+    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS, VL, WD>),
+                       dim3((unsigned)(fg.ncb * p.n_strips)),
+                       dim3(FusedCfg<TAPS, T, WD>::BW * kWave), lds, st, gy, x, w, mask, gx,
+                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, fg.ncb, fg.n_sp, is, ahead,
+                       lim_lds);
+    return hipGetLastError();
+}
+
+template <int DT, bool M, bool T, int TAPS, bool VL>
+hipError_t launch_fused_layout(bool wide, const Plan &p, const void *gy, const void *x,
+                               const void *w, const uint8_t *mask, void *gx, void *ws,
+                               hipStream_t st, size_t lds, const InStrides &is,
+                               const uint8_t *ahead, int lim_lds) {
+    if constexpr (TAPS <= 3 && !VL) {
+        if (wide)
+            return launch_fused<DT, M, T, TAPS, VL, true>(p, gy, x, w, mask, gx, ws, st, lds, is,
+                                                          ahead, lim_lds);
+    }
+    return launch_fused<DT, M, T, TAPS, VL, false>(p, gy, x, w, mask, gx, ws, st, lds, is, ahead,
+                                                   lim_lds);
+}
+
+// One fused launch for any (mask, strided, W) of the padded layouts (VL false) or the packed one.
+template <int DT, bool VL>
+hipError_t launch_fused_any(const Plan &p, const void *gy, const void *x, const void *w,
+                            const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
+                            const InStrides &is, bool strided, const uint8_t *ahead = nullptr,
+                            int lim_lds = 0) {
+    const bool wide = !VL && fused_wide(p.C, p.W);
+#define MCCB_FUSED(M, T, TAPS)                                                                    \
+    return launch_fused_layout<DT, M, T, TAPS, VL>(wide, p, gy, x, w, mask, gx, ws, st, lds, is,  \
+                                                   ahead, lim_lds)
+#define MCCB_FUSED_W(TAPS)                                                                        \
+    if constexpr (!VL) {                                                                          \
+        if (strided) {                                                                            \
+            if (mask) MCCB_FUSED(true, true, TAPS);                                               \
+            MCCB_FUSED(false, true, TAPS);                                                        \
+        }                                                                                         \
+    }                                                                                             \
+    if (mask) MCCB_FUSED(true, false, TAPS);                                                      \
+    MCCB_FUSED(false, false, TAPS);
+    switch (p.W) {
+        case 1: MCCB_FUSED_W(1)
+        case 2: MCCB_FUSED_W(2)
+        case 3: MCCB_FUSED_W(3)
+        case 4: MCCB_FUSED_W(4)
+        default: return hipErrorInvalidValue;
+    }
+#undef MCCB_FUSED_W
+#undef MCCB_FUSED
 }
 
 template <int DT>
@@ -862,31 +1027,7 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     const size_t lds_floor = MCCB_LDS_FLOOR;
     const size_t lds = mask ? (p.mask_lds > lds_floor ? p.mask_lds : lds_floor) : lds_floor;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
-#define MCCB_FUSED(M, T, TAPS)                                                                    \
-    do {                                                                                          \
-        constexpr int cg = fused_col_groups(T, TAPS);                                             \
-        const int64_t ncb = col_blocks(p.C, cg);                                                  \
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS>), dim3((unsigned)(ncb * p.n_strips)),  \
-                           dim3(cg * kRing * kWave), lds, st, (const vec_t *)gy, (const vec_t *)x, \
-                           (const vec_t *)w, mask, (vec_t *)gx, (double *)ws, p.S, p.B, p.H,      \
-                           p.rows_per_strip, ncb, is);                                            \
-    } while (0)
-#define MCCB_FUSED_W(TAPS)                                                                        \
-    if (mask) {                                                                                   \
-        if (strided) MCCB_FUSED(true, true, TAPS); else MCCB_FUSED(true, false, TAPS);            \
-    } else {                                                                                      \
-        if (strided) MCCB_FUSED(false, true, TAPS); else MCCB_FUSED(false, false, TAPS);          \
-    }
-    switch (p.W) {
-        case 1: MCCB_FUSED_W(1); break;
-        case 2: MCCB_FUSED_W(2); break;
-        case 3: MCCB_FUSED_W(3); break;
-        case 4: MCCB_FUSED_W(4); break;
-        default: return hipErrorInvalidValue;
-    }
-#undef MCCB_FUSED_W
-#undef MCCB_FUSED
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_fused_any<DT, false>(p, gy, x, w, mask, gx, ws, st, lds, is, strided);
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hipErrorInvalidValue;
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
@@ -974,7 +1115,7 @@ bool inplace3(const View3 &v, int vec, int64_t H, uint64_t span_limit) {
           ((uintptr_t)v.p % (uintptr_t)(vec * 2)) == 0))
         return false;
     if (span_limit == 0) return true;
-    const int64_t extra_batches = (kBlockCols - 1) / H + 1;  // j - (block's first batch), at most
+    const int64_t extra_batches = (kMaxGroupCols - 1) / H + 1;  // j - (wave's first batch), at most
     const unsigned __int128 rel = ((unsigned __int128)extra_batches * (uint64_t)v.s1 + (uint64_t)H) * 2u;
     return rel < span_limit;
 }
@@ -1092,28 +1233,7 @@ hipError_t launch_varlen_bwd(const Plan &p, const void *gy, const void *x, const
     const int lim_lds = mask ? (int)p.mask_lds : 0;
     const size_t lds = (size_t)lim_lds + (size_t)span;
     const InStrides is{p.H, p.H, p.H, p.H, T, 1};
-#define MCCB_VL(M, TAPS)                                                                          \
-    do {                                                                                          \
-        constexpr int cg = fused_col_groups(false, TAPS);                                         \
-        const int64_t ncb = col_blocks(p.C, cg);                                                  \
-        hipLaunchKernelGGL((mccb_fused_bwd<DT, M, false, TAPS, true>),                            \
-                           dim3((unsigned)(ncb * p.n_strips)), dim3(cg * kRing * kWave), lds, st, \
-                           (const vec_t *)gy, (const vec_t *)x, (const vec_t *)w, mask,           \
-                           (vec_t *)gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip, ncb, is,   \
-                           ahead, lim_lds);                                                       \
-    } while (0)
-#define MCCB_VL_W(TAPS)                                                                           \
-    if (mask) MCCB_VL(true, TAPS); else MCCB_VL(false, TAPS);
-    switch (p.W) {
-        case 1: MCCB_VL_W(1); break;
-        case 2: MCCB_VL_W(2); break;
-        case 3: MCCB_VL_W(3); break;
-        case 4: MCCB_VL_W(4); break;
-        default: return hipErrorInvalidValue;
-    }
-#undef MCCB_VL_W
-#undef MCCB_VL
-    e = hipGetLastError();
+    e = launch_fused_any<DT, true>(p, gy, x, w, mask, gx, ws, st, lds, is, false, ahead, lim_lds);
     if (e != hipSuccess) return e;
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
@@ -1197,13 +1317,16 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     const int rc = check_shape(S, B, H, dtype);
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype);
+    const bool wide = fused_wide(p.C, 3);
+    typedef FusedCfg<3, false, true> Wd;
+    typedef FusedCfg<3, false, false> Rg;
     plan->rows_per_turn = kTurnRows;
-    plan->rows_per_round = kRoundRows;
+    plan->rows_per_round = wide ? Wd::RR : Rg::RR;
     plan->rows_per_strip = p.rows_per_strip;
     plan->n_strips = p.n_strips;
-    plan->cols_per_block = kBlockCols;
-    plan->n_col_blocks = p.n_col_blocks;
-    plan->waves_per_block = kBlockWaves;
+    plan->cols_per_block = wide ? Wd::CG * Wd::GC : Rg::CG * Rg::GC;
+    plan->n_col_blocks = wide ? fused_grid<3, false, true>(p.C).ncb : fused_grid<3, false, false>(p.C).ncb;
+    plan->waves_per_block = wide ? Wd::BW : Rg::BW;
     plan->workspace_size = p.ws_bytes;
     const FwdPlan f = make_fwd_plan(S, B, H);
     plan->fwd_rows_per_tile = f.rows;
@@ -1285,7 +1408,7 @@ int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *wei
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype, (int)W);
     *workspace_size =
-        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan).total;
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(B * H, W), kLaneSpan).total;
     return MCCB_OK;
 }
 
@@ -1302,7 +1425,7 @@ int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype, (int)W);
     const ExLayout L =
-        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, kVec, kLaneSpan);
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(B * H, W), kLaneSpan);
     if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
     if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
     if (!aligned16(gradX) || !aligned16(gradWeight) || (L.total > 0 && !aligned16(workspace)))
