@@ -226,7 +226,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed calls before each timed leg (the backward reaches its steady "
+                         "duration after about ten calls)")
     ap.add_argument("--workload", type=int, default=None,
                     help="index into synth.WORKLOADS (default: the B*S=512K H=5120 workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -120,6 +120,10 @@ constexpr int kWave = 64;  // lanes per wavefront on CDNA
 constexpr int kTurnRows = MCCB_TURN_ROWS;
 constexpr int kPlanRound = 16;  // strips are a whole number of this many rows (any layout's round)
 constexpr int kPlanMaxStripRows = 784;  // longest strip the plan makes for S >= 768 (sizing only)
+// Bytes a staged mask slot holds beyond the strip's rows: a whole turn (kTurnRows + W - 1 <= 16
+// rows, starting 8-aligned) reads 16 bytes, so the last one reaches 8 bytes past the strip.
+constexpr int kMaskPad = 8;
+static_assert(kTurnRows == 8 && kTurnRows + 3 <= 16, "a turn's mask bytes are two 8-byte words");
 constexpr int kReduceWaves = 16;        // wavefronts per reduce block
 constexpr int kReduceCols = kWave * 2;  // channels per reduce block (2 fp64 per lane)
 
@@ -336,7 +340,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
     constexpr int V = Cfg::V, CG = Cfg::CG, RG = Cfg::RG, TR = kTurnRows, RR = Cfg::RR;
     typedef typename Vec<V>::t vec_t;
     constexpr int L = W - 1;  // look-ahead rows
-    extern __shared__ uint8_t smask[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t smask[];
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane of a wave; saying so keeps everything derived from
@@ -361,13 +365,17 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
     const int64_t h = c - j * H;
     const int64_t jg = ((v0 < CV ? v0 : CV - 1) * V) / H;  // the wave's first batch
 
-    const int span = (int)(rows_per_strip + L);  // staged rows of the strip
+    const int span = (int)(rows_per_strip + L);  // rows of the strip and its look-ahead
+    const int mspan = (int)(rows_per_strip + kMaskPad);  // bytes of one staged mask slot
     int moff = 0;  // offset of this lane's batch in the staged mask
     if constexpr (HAS_MASK) {
-        // Each column group stages the bytes of its (at most two) batches: [CG][2][span]; the
-        // second slot only when the group's columns reach into the next batch. A thread issues
-        // the loads of a batch of its bytes before writing any of them to LDS, so that it waits
-        // once per batch instead of once per byte.
+        // Each column group stages the bytes of its (at most two) batches: [CG][2][mspan], 0xFF
+        // where the mask keeps the row and 0 where it drops it (or the row is past S); the second
+        // slot only when the group's columns reach into the next batch. A slot is a multiple of 8
+        // bytes and holds 8 bytes past the strip's look-ahead, so that a whole turn reads its
+        // rows' bytes as two aligned 8-byte words. A thread issues the loads of a batch of its
+        // bytes before writing any of them to LDS, so that it waits once per batch instead of
+        // once per byte.
         int64_t jf[CG];
         bool two[CG];
 #pragma unroll
@@ -378,16 +386,17 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
             two[gg] = (vb * V + V - 1) / H != jf[gg];
         }
         auto mask_byte = [&](int t) -> uint8_t {
-            const int slot = t / span;  // group * 2 + batch within the group
+            const int slot = t / mspan;  // group * 2 + batch within the group
             const int gg = slot >> 1;
             if ((slot & 1) && !two[gg]) return 0;
             const int64_t jj = jf[gg] + (slot & 1);
-            const int64_t row = rs0 + (t - slot * span);
-            return (row < S) ? mask[jj * st.m_batch + row * st.m_row] : (uint8_t)0;
+            const int64_t row = rs0 + (t - slot * mspan);
+            return (row < S && mask[jj * st.m_batch + row * st.m_row] != 0) ? (uint8_t)0xFF
+                                                                              : (uint8_t)0;
         };
         constexpr int kThreads = Cfg::BW * kWave;
-        constexpr int kStage = (2 * CG * (kPlanMaxStripRows + 3) + kThreads - 1) / kThreads;
-        const int n = CG * 2 * span;
+        constexpr int kStage = (2 * CG * (kPlanMaxStripRows + kMaskPad) + kThreads - 1) / kThreads;
+        const int n = CG * 2 * mspan;
         for (int base = 0; base < n; base += kStage * kThreads) {
             uint8_t vals[kStage];
 #pragma unroll
@@ -401,7 +410,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
                 if (t < n) smask[t] = vals[q];
             }
         }
-        moff = (group * 2 + (int)(j - jg)) * span;
+        moff = (group * 2 + (int)(j - jg)) * mspan;
         if constexpr (!VARLEN) __syncthreads();
     }
     if constexpr (VARLEN) {
@@ -440,6 +449,28 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
     auto keep = [&](int64_t row) -> bool {
         if constexpr (HAS_MASK) return smask[moff + (int)(row - rs0)] != 0;
         return true;
+    };
+    // A whole turn's mask: the staged bytes of rows i0 .. i0+15 (i0 - rs0 is a multiple of 8);
+    // `masked(q, mw, k)` is gradY row i0+k's lane vector with every word cleared where the mask
+    // drops the row (the byte, sign-extended, is the word mask).
+    auto turn_mask = [&](int64_t i0, uint32_t (&mw)[4]) {
+        if constexpr (HAS_MASK) {
+            const uint8_t *mp = smask + moff + (int)(i0 - rs0);
+            const uint2 lo = *reinterpret_cast<const uint2 *>(mp);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(mp + 8);
+            mw[0] = lo.x;
+            mw[1] = lo.y;
+            mw[2] = hi.x;
+            mw[3] = hi.y;
+        }
+    };
+    auto masked = [&](const vec_t &q, const uint32_t (&mw)[4], int k) -> vec_t {
+        if constexpr (!HAS_MASK) return q;
+        const uint32_t m = (uint32_t)((int32_t)(mw[k >> 2] << (24 - 8 * (k & 3))) >> 24);
+        vec_t r;
+#pragma unroll
+        for (int p = 0; p < V / 2; ++p) r[p] = q[p] & m;
+        return r;
     };
 
     // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
@@ -485,12 +516,14 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
     };
     auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
         const int64_t i0 = r0 + ring * TR;
+        uint32_t mw[4];
+        turn_mask(i0, mw);
         double d[W][V];
 #pragma unroll
-        for (int k = 0; k < L; ++k) widen<DT, V>(keep(i0 + k) ? qy[k] : zero, d[k]);
+        for (int k = 0; k < L; ++k) widen<DT, V>(masked(qy[k], mw, k), d[k]);
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
-            widen<DT, V>(keep(i0 + L + u) ? qy[u + L] : zero, d[L]);
+            widen<DT, V>(masked(qy[u + L], mw, u + L), d[L]);
             vec_t r;
             if constexpr (VARLEN) {
                 // a uniform branch: only the last W-1 rows of a sequence take the limited form
@@ -908,7 +941,7 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype, int W = 3) {
     for (;;) {
         const int64_t rows = (S + strips - 1) / strips;
         p.rows_per_strip = (rows + kPlanRound - 1) / kPlanRound * kPlanRound;
-        p.mask_lds = (size_t)kMaxStagedBatches * (size_t)(p.rows_per_strip + W - 1);
+        p.mask_lds = (size_t)kMaxStagedBatches * (size_t)(p.rows_per_strip + kMaskPad);
         if (p.mask_lds <= (size_t)kMaxMaskLds || strips >= max_strips) break;
         ++strips;  // keep the staged mask within its LDS budget
     }
