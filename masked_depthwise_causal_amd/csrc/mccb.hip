@@ -78,6 +78,12 @@
 #ifndef MCCB_NT_LOAD
 #define MCCB_NT_LOAD 1  // streaming (non-temporal) hint on gradY / x loads read once
 #endif
+#ifndef MCCB_NT_GY
+#define MCCB_NT_GY 1  // ... also on the gradY rows of a backward turn that no other turn reads
+#endif
+#ifndef MCCB_FWD_NT_X
+#define MCCB_FWD_NT_X 1  // ... and on the x rows of a forward tile that no other tile reads
+#endif
 #ifndef MCCB_NT_STORE
 #define MCCB_NT_STORE 1  // streaming (non-temporal) hint on gradX stores
 #endif
@@ -165,6 +171,9 @@ constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
 constexpr int64_t kMinW = 1, kMaxW = 4;  // window taps supported by the kernels
 constexpr int64_t kStripRows = MCCB_STRIP_ROWS;
+// A strip is at most kStripRows rows rounded up to a whole round; the fused kernel's mask
+// staging is unrolled for strips of up to kPlanMaxStripRows rows.
+static_assert(kStripRows + kPlanRound - 1 <= kPlanMaxStripRows, "strips longer than the staging");
 constexpr int64_t kMinBlocks = MCCB_MIN_BLOCKS;
 constexpr int64_t kMinStripRows = MCCB_MIN_STRIP_ROWS;
 constexpr int64_t kMaxMaskLds = 48 * 1024;  // bytes of LDS for the staged mask, at most
@@ -235,6 +244,24 @@ __device__ static inline T load_vec(const T *p) {
 template <typename T>
 __device__ static inline T load_vec_cached(const T *p) {
     return *p;
+}
+// gradY rows a turn of the fused kernel reads once (neither look-ahead row of a turn)
+template <typename T>
+__device__ static inline T load_gy_stream(const T *p) {
+#if MCCB_NT_GY
+    return load_vec(p);
+#else
+    return *p;
+#endif
+}
+// x rows of a forward tile that no other tile reads (not the tile's last W-1 rows)
+template <typename T>
+__device__ static inline T load_fwd_stream(const T *p) {
+#if MCCB_FWD_NT_X
+    return load_vec(p);
+#else
+    return *p;
+#endif
 }
 template <typename T>
 __device__ static inline void store_vec(T *p, T v) {
@@ -373,9 +400,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
         // where the mask keeps the row and 0 where it drops it (or the row is past S); the second
         // slot only when the group's columns reach into the next batch. A slot is a multiple of 8
         // bytes and holds 8 bytes past the strip's look-ahead, so that a whole turn reads its
-        // rows' bytes as two aligned 8-byte words. A thread issues the loads of a batch of its
-        // bytes before writing any of them to LDS, so that it waits once per batch instead of
-        // once per byte.
+        // rows' bytes as two aligned 8-byte words. A thread loads all of its bytes from clamped,
+        // always valid addresses before it writes any of them to LDS, and decides afterwards
+        // which of them count: no load depends on a branch, so they issue back to back and the
+        // thread waits once instead of once per byte.
         int64_t jf[CG];
         bool two[CG];
 #pragma unroll
@@ -385,29 +413,31 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
             jf[gg] = (va * V) / H;
             two[gg] = (vb * V + V - 1) / H != jf[gg];
         }
-        auto mask_byte = [&](int t) -> uint8_t {
-            const int slot = t / mspan;  // group * 2 + batch within the group
-            const int gg = slot >> 1;
-            if ((slot & 1) && !two[gg]) return 0;
-            const int64_t jj = jf[gg] + (slot & 1);
-            const int64_t row = rs0 + (t - slot * mspan);
-            return (row < S && mask[jj * st.m_batch + row * st.m_row] != 0) ? (uint8_t)0xFF
-                                                                              : (uint8_t)0;
-        };
+        // Slot (gg, b) holds bytes rs0 .. rs0+mspan-1 of mask row jf[gg] + b; a thread takes bytes
+        // tid, tid + kThreads, ... of every slot. The slot's batch is the same for the whole block.
         constexpr int kThreads = Cfg::BW * kWave;
-        constexpr int kStage = (2 * CG * (kPlanMaxStripRows + kMaskPad) + kThreads - 1) / kThreads;
-        const int n = CG * 2 * mspan;
-        for (int base = 0; base < n; base += kStage * kThreads) {
-            uint8_t vals[kStage];
+        constexpr int kPer = (kPlanMaxStripRows + kMaskPad + kThreads - 1) / kThreads;
+        uint8_t vals[2 * CG][kPer];
 #pragma unroll
-            for (int q = 0; q < kStage; ++q) {
-                const int t = base + q * kThreads + (int)threadIdx.x;
-                vals[q] = (t < n) ? mask_byte(t) : (uint8_t)0;
+        for (int slot = 0; slot < 2 * CG; ++slot) {
+            const int gg = slot >> 1;
+            const bool second = (slot & 1) != 0;
+            const uint8_t *src = mask + (jf[gg] + ((second && two[gg]) ? 1 : 0)) * st.m_batch;
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int64_t row = rs0 + (int)threadIdx.x + q * kThreads;
+                vals[slot][q] = src[(row < S ? row : S - 1) * st.m_row];
             }
+        }
 #pragma unroll
-            for (int q = 0; q < kStage; ++q) {
-                const int t = base + q * kThreads + (int)threadIdx.x;
-                if (t < n) smask[t] = vals[q];
+        for (int slot = 0; slot < 2 * CG; ++slot) {
+            const bool used = (slot & 1) == 0 || two[slot >> 1];
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int t = (int)threadIdx.x + q * kThreads;
+                if (t < mspan)
+                    smask[slot * mspan + t] =
+                        (used && rs0 + t < S && vals[slot][q] != 0) ? (uint8_t)0xFF : (uint8_t)0;
             }
         }
         moff = (group * 2 + (int)(j - jg)) * mspan;
@@ -503,16 +533,18 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
     // first L gradY rows were the previous turn's last look-ahead rows (this wave's own with one
     // wave per group, the other ring wave's otherwise), and this turn's last L are the next turn's
     // first: cached loads, so those come from L2; the rest stream.
+    // (Each kind of load has a loop of its own: a choice between a cached and a streaming load
+    // of one address inside one loop body is merged into a single plain load by the compiler.)
     auto issue = [&](int64_t r0, vec_t (&qy)[TR + L], vec_t (&qx)[TR]) {
         const int64_t i0 = r0 + ring * TR;
 #pragma unroll
         for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(at_gy(i0 + k));
 #pragma unroll
-        for (int u = 0; u < TR; ++u) {
-            qy[u + L] = (u + L >= TR) ? load_vec_cached(at_gy(i0 + L + u))
-                                      : load_vec(at_gy(i0 + L + u));
-            qx[u] = load_vec(at_x(i0 + u));
-        }
+        for (int u = 0; u < TR - L; ++u) qy[u + L] = load_gy_stream(at_gy(i0 + L + u));
+#pragma unroll
+        for (int u = TR - L; u < TR; ++u) qy[u + L] = load_vec_cached(at_gy(i0 + L + u));
+#pragma unroll
+        for (int u = 0; u < TR; ++u) qx[u] = load_vec(at_x(i0 + u));
     };
     auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
         const int64_t i0 = r0 + ring * TR;
@@ -740,42 +772,104 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     const int64_t j = c0 / H;
     const int64_t r0 = (rt * (kFwdWaves >> cw_log2) + wr) * kFwdRows;  // may be >= S: rows guarded
 
-    // x rows r0-L .. r0+kFwdRows-1; rows outside [0, S) are zero
-    fvec_t xr[kFwdRows + L];
-#pragma unroll
-    for (int u = 0; u < kFwdRows + L; ++u) {
-        const int64_t row = r0 - L + u;
-        fvec_t q = {};
-        if (row >= 0 && row < S) {
-            const fvec_t *p = STRIDED ? reinterpret_cast<const fvec_t *>(
-                                            reinterpret_cast<const char *>(x) +
-                                            (row * st.x_row + j * st.x_batch + h0) * 2)
-                                      : x + row * CV + v;
-            q = (u < L || u >= kFwdRows) ? *p : __builtin_nontemporal_load(p);
-        }
-        xr[u] = q;
-    }
+    // Loads are issued before any of them is used, weights first (the first rows' arithmetic
+    // needs them), then the mask, then the x rows.
+    //
     // Weights: fp64 copies take 2*W*kFwdVec registers for the whole tile. The 4-tap and the
     // packed-layout instantiations, which need the room, keep them in fp32 (exact for 16-bit
     // values) and widen them at each use instead; the others keep fp64 copies, which measured
     // faster for them.
     constexpr bool kNarrowW = W > 3 || VARLEN;
     typedef typename std::conditional<kNarrowW, float, double>::type wt_t;
+    fvec_t wq[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) wq[k] = w[(k * H + h0) / kFwdVec];
+
+    // Mask of the tile's rows as words of bytes, byte u for row r0+u: 0xFF keeps the row, 0 drops
+    // it (or the row is past S); it clears the packed output words of dropped rows. When the
+    // tile's bytes are contiguous and 8-byte aligned (unit row stride, batch stride and base
+    // multiples of 8, all rows inside S; the same answer on every lane of the wave) they arrive as
+    // one 8-byte load per lane, as raw bytes (any nonzero byte keeps its row) turned into 0xFF / 0
+    // once the x loads are issued; otherwise byte by byte from clamped addresses, loaded without a
+    // branch so that the loads issue together.
+    constexpr int kMaskWords = (kFwdRows + 3) / 4;
+    uint32_t mk[kMaskWords];
+#pragma unroll
+    for (int q = 0; q < kMaskWords; ++q) mk[q] = ~0u;
+    if constexpr (HAS_MASK) {
+        const uint8_t *mcol = mask + j * st.m_batch;
+        const bool vec_ok = kFwdRows == 8 && st.m_row == 1 && (st.m_batch & 7) == 0 &&
+                            (reinterpret_cast<uintptr_t>(mask) & 7) == 0 && r0 + kFwdRows <= S;
+        if (vec_ok) {
+            const uint2 mb = load_vec_cached(reinterpret_cast<const uint2 *>(mcol + r0));
+            mk[0] = mb.x;
+            mk[kMaskWords > 1 ? 1 : 0] = mb.y;
+        } else {
+            uint8_t mbyte[kFwdRows];
+#pragma unroll
+            for (int u = 0; u < kFwdRows; ++u)
+                mbyte[u] = mcol[((r0 + u < S) ? r0 + u : S - 1) * st.m_row];
+#pragma unroll
+            for (int q = 0; q < kMaskWords; ++q) mk[q] = 0u;
+#pragma unroll
+            for (int u = 0; u < kFwdRows; ++u)
+                mk[u / 4] |= (r0 + u < S && mbyte[u] != 0) ? 0xFFu << (8 * (u % 4)) : 0u;
+        }
+    }
+
+    // x rows r0-L .. r0+kFwdRows-1; rows outside [0, S) are zero. The look-back rows and the
+    // tile's last L rows (the next tile's look-back) are cached loads, the rest stream. Tiles whose
+    // rows all exist (all but the first and the last, a uniform test) load without a branch per
+    // row.
+    fvec_t xr[kFwdRows + L];
+    auto x_at = [&](int64_t row) -> const fvec_t * {
+        return STRIDED ? reinterpret_cast<const fvec_t *>(reinterpret_cast<const char *>(x) +
+                                                           (row * st.x_row + j * st.x_batch + h0) * 2)
+                       : x + row * CV + v;
+    };
+    // (Each kind of load has a loop of its own: a choice between a cached and a streaming load
+    // of one address inside one loop body is merged into a single plain load by the compiler.)
+    if (r0 >= L && r0 + kFwdRows <= S) {
+#pragma unroll
+        for (int u = 0; u < L; ++u) xr[u] = load_vec_cached(x_at(r0 - L + u));
+#pragma unroll
+        for (int u = L; u < kFwdRows; ++u) xr[u] = load_fwd_stream(x_at(r0 - L + u));
+#pragma unroll
+        for (int u = kFwdRows; u < kFwdRows + L; ++u) xr[u] = load_vec_cached(x_at(r0 - L + u));
+    } else {
+        auto guarded = [&](int u, bool stream) {
+            const int64_t row = r0 - L + u;
+            fvec_t q = {};
+            if (row >= 0 && row < S) q = stream ? load_fwd_stream(x_at(row)) : load_vec_cached(x_at(row));
+            xr[u] = q;
+        };
+#pragma unroll
+        for (int u = 0; u < L; ++u) guarded(u, false);
+#pragma unroll
+        for (int u = L; u < kFwdRows; ++u) guarded(u, true);
+#pragma unroll
+        for (int u = kFwdRows; u < kFwdRows + L; ++u) guarded(u, false);
+    }
+    if constexpr (HAS_MASK) {
+        // any nonzero byte keeps its row: set each byte's top bit where the byte is nonzero (no
+        // carry crosses a byte), then widen that bit to the whole byte (0xFF stays 0xFF)
+#pragma unroll
+        for (int q = 0; q < kMaskWords; ++q) {
+            const uint32_t t = (((mk[q] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | mk[q]) & 0x80808080u;
+            mk[q] = (t >> 7) * 0xFFu;
+        }
+    }
     wt_t wt[W][kFwdVec];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        const fvec_t q = w[(k * H + h0) / kFwdVec];
 #pragma unroll
         for (int p = 0; p < kFwdWords; ++p) {
             float lo, hi;
-            Fmt<DT>::unpack(q[p], lo, hi);
+            Fmt<DT>::unpack(wq[k][p], lo, hi);
             wt[k][2 * p] = lo;
             wt[k][2 * p + 1] = hi;
         }
     }
-    uint8_t keep[kFwdRows];
-#pragma unroll
-    for (int u = 0; u < kFwdRows; ++u) keep[u] = 1;
     // VARLEN: rows of the tile whose window reaches into another sequence. If the tile's last row
     // has at least kFwdRows-1+L earlier rows in its sequence, no row of the tile does, and the
     // tile takes the unlimited form (a uniform branch; only tiles at sequence starts do not).
@@ -791,11 +885,6 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
         const int b = (r0 + u < S) ? (int)behind[r0 + u] : L;
         return __builtin_amdgcn_readfirstlane(L - (b < L ? b : L));
     };
-    if (HAS_MASK) {
-        const uint8_t *mrow = mask + j * st.m_batch + r0 * st.m_row;
-#pragma unroll
-        for (int u = 0; u < kFwdRows; ++u) keep[u] = (r0 + u < S) ? mrow[u * st.m_row] : 0;
-    }
 
     double win[W][kFwdVec];  // win[k] = x row i-L+k
 #pragma unroll
@@ -831,11 +920,13 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
             double s = win[0][e] * (double)wt[0][e];
 #pragma unroll
             for (int k = 1; k < W; ++k) s = __builtin_fma(win[k][e], (double)wt[k][e], s);
-            out[e] = keep[u] ? round_to_odd_f32(s) : 0.0f;
+            out[e] = round_to_odd_f32(s);
         }
+        // all ones where the mask keeps row r0+u, zero (+0.0 in both halves) where it drops it
+        const uint32_t keep = (uint32_t)((int32_t)(mk[u / 4] << (24 - 8 * (u % 4))) >> 24);
         fvec_t r;
 #pragma unroll
-        for (int p = 0; p < kFwdWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]);
+        for (int p = 0; p < kFwdWords; ++p) r[p] = Fmt<DT>::pack(out[2 * p], out[2 * p + 1]) & keep;
         if (row < S) __builtin_nontemporal_store(r, y + row * CV + v);
 #pragma unroll
         for (int k = 0; k < L; ++k)
