@@ -84,6 +84,9 @@
 #ifndef MCCB_FWD_NT_X
 #define MCCB_FWD_NT_X 1  // ... and on the x rows of a forward tile that no other tile reads
 #endif
+#ifndef MCCB_REDUCE_VEC
+#define MCCB_REDUCE_VEC 1  // gradWeight reduction: channels per lane (1: more blocks across the CUs)
+#endif
 #ifndef MCCB_NT_STORE
 #define MCCB_NT_STORE 1  // streaming (non-temporal) hint on gradX stores
 #endif
@@ -131,7 +134,9 @@ constexpr int kPlanMaxStripRows = 784;  // longest strip the plan makes for S >=
 constexpr int kMaskPad = 8;
 static_assert(kTurnRows == 8 && kTurnRows + 3 <= 16, "a turn's mask bytes are two 8-byte words");
 constexpr int kReduceWaves = 16;        // wavefronts per reduce block
-constexpr int kReduceCols = kWave * 2;  // channels per reduce block (2 fp64 per lane)
+constexpr int kReduceVec = MCCB_REDUCE_VEC;          // channels per reduce lane (1 or 2)
+constexpr int kReduceCols = kWave * kReduceVec;      // channels per reduce block
+static_assert(kReduceVec == 1 || kReduceVec == 2, "reduce lanes own 1 or 2 channels");
 
 // Lane vector of V 16-bit values (V/2 words): one load per row.
 template <int V>
@@ -657,44 +662,74 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
 // ---------------------------------------------------------------------------------------------
 // Kernel 2: gradWeight[k,h] = sum over strips s (outer) and batches j (inner) of
 // ws[s][k][j*H + h], in fp64, then one rounding to the dtype.
-// grid = (ceil(H / 128), W), block = kReduceWaves * 64 lanes; a lane owns 2 channels. Each wave
-// sums a contiguous range of the (s, j) rows; the waves' sums are then added in wave order.
+// grid = (ceil(H / kReduceCols), W), block = kReduceWaves * 64 lanes; a lane owns kReduceVec
+// channels. Each wave sums a contiguous range of the (s, j) rows; the waves' sums are then added
+// in wave order. The order of every channel's sum depends only on (n_strips, B), not on
+// kReduceVec.
 // ---------------------------------------------------------------------------------------------
 template <int DT>
+__device__ static inline void store_gw(uint16_t *p, double t) {
+    *p = (uint16_t)(Fmt<DT>::pack(round_to_odd_f32(t), 0.0f) & 0xFFFFu);
+}
+template <int DT>
+__device__ static inline void store_gw(uint16_t *p, f64x2 t) {  // p 4-byte aligned
+    *reinterpret_cast<uint32_t *>(p) = Fmt<DT>::pack(round_to_odd_f32(t[0]), round_to_odd_f32(t[1]));
+}
+
+template <int DT>
 __global__ void __launch_bounds__(kReduceWaves *kWave)
-    mccb_gw_reduce(const double *__restrict__ ws, uint32_t *__restrict__ gw, int64_t n_strips,
+    mccb_gw_reduce(const double *__restrict__ ws, uint16_t *__restrict__ gw, int64_t n_strips,
                    int64_t B, int64_t H) {
-    __shared__ f64x2 red[kReduceWaves][kWave];
+    constexpr int RV = kReduceVec;
+    typedef typename std::conditional<RV == 2, f64x2, double>::type rvec_t;
+    __shared__ rvec_t red[kReduceWaves][kWave];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int k = blockIdx.y;
     const int W = gridDim.y;  // taps
-    const int64_t h = (int64_t)blockIdx.x * kReduceCols + lane * 2;
+    const int64_t h = (int64_t)blockIdx.x * kReduceCols + lane * RV;
     const int64_t C = B * H;
     const int64_t rows = n_strips * B;
     const int64_t per = (rows + kReduceWaves - 1) / kReduceWaves;
     const int64_t lo = wave * per;
     const int64_t hi = (lo + per < rows) ? lo + per : rows;
 
-    f64x2 acc = {0.0, 0.0};
+    // The wave's rows in order, kBatch loads in flight at a time. `off` (the same on every lane)
+    // is the element offset of row r's partials: row (s, j) sits at (s*W + k)*C + j*H. It stops
+    // at the wave's last row, so the loads past it re-read that row (always in bounds) and are
+    // not added.
+    constexpr int kBatch = 16;
+    rvec_t acc = {};
     if (h < H && lo < hi) {
-        int64_t s = lo / B, jj = lo - (lo / B) * B;
-#pragma unroll 4
-        for (int64_t r = lo; r < hi; ++r) {
-            acc += *reinterpret_cast<const f64x2 *>(ws + (s * W + k) * C + jj * H + h);
-            if (++jj == B) {
-                jj = 0;
-                ++s;
+        int64_t jj = lo % B;
+        int64_t off = ((lo / B) * W + k) * C + jj * H;
+        const int64_t wrap = W * C - (B - 1) * H;  // from (s, B-1) to (s+1, 0)
+        const double *base = ws + h;
+        for (int64_t r = lo; r < hi; r += kBatch) {
+            rvec_t v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                v[q] = *reinterpret_cast<const rvec_t *>(base + off);
+                if (r + q + 1 < hi) {
+                    if (++jj == B) {
+                        jj = 0;
+                        off += wrap;
+                    } else {
+                        off += H;
+                    }
+                }
             }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (r + q < hi) acc += v[q];
         }
     }
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && h < H) {
-        f64x2 t = red[0][lane];
+        rvec_t t = red[0][lane];
         for (int q = 1; q < kReduceWaves; ++q) t += red[q][lane];
-        // gradWeight[k, h .. h+1]: one 32-bit word at element offset k*H + h (h even).
-        gw[(k * H + h) / 2] = Fmt<DT>::pack(round_to_odd_f32(t[0]), round_to_odd_f32(t[1]));
+        store_gw<DT>(gw + k * H + h, t);  // gradWeight[k, h ..]: one rounding per channel
     }
 }
 
@@ -1157,7 +1192,7 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
-                       (uint32_t *)gw, p.n_strips, p.B, p.H);
+                       (uint16_t *)gw, p.n_strips, p.B, p.H);
     e = hipGetLastError();
     if (e == hipSuccess && ev && hipEventRecord(ev[2], st) != hipSuccess) return hipErrorInvalidValue;
     return e;
@@ -1362,7 +1397,7 @@ hipError_t launch_varlen_bwd(const Plan &p, const void *gy, const void *x, const
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
-                       (uint32_t *)gw, p.n_strips, p.B, p.H);
+                       (uint16_t *)gw, p.n_strips, p.B, p.H);
     return hipGetLastError();
 }
 
