@@ -97,7 +97,7 @@
 #define MCCB_LDS_FLOOR 0  // dynamic LDS bytes the fused kernel reserves at least (caps blocks per CU)
 #endif
 #ifndef MCCB_STRIP_ROWS
-#define MCCB_STRIP_ROWS 768  // the plan aims for strips about this many rows long ...
+#define MCCB_STRIP_ROWS 1024  // the plan aims for strips about this many rows long ...
 #endif
 #ifndef MCCB_MIN_BLOCKS
 #define MCCB_MIN_BLOCKS 2048  // ... splitting further until the grid has this many blocks ...
@@ -128,7 +128,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;  // lanes per wavefront on CDNA
 constexpr int kTurnRows = MCCB_TURN_ROWS;
 constexpr int kPlanRound = 16;  // strips are a whole number of this many rows (any layout's round)
-constexpr int kPlanMaxStripRows = 784;  // longest strip the plan makes for S >= 768 (sizing only)
+// Longest strip the plan makes: ceil(S / ceil(S / MCCB_STRIP_ROWS)) <= MCCB_STRIP_ROWS rows,
+// rounded up to a whole round (the mask staging is unrolled for it).
+constexpr int kPlanMaxStripRows = (MCCB_STRIP_ROWS + kPlanRound - 1) / kPlanRound * kPlanRound;
 // Bytes a staged mask slot holds beyond the strip's rows: a whole turn (kTurnRows + W - 1 <= 16
 // rows, starting 8-aligned) reads 16 bytes, so the last one reaches 8 bytes past the strip.
 constexpr int kMaskPad = 8;
@@ -176,9 +178,7 @@ constexpr int64_t kMinH = 384, kMaxH = 24576, kHAlign = 64;
 constexpr int64_t kMaxB = 32, kMaxBS = 524288;
 constexpr int64_t kMinW = 1, kMaxW = 4;  // window taps supported by the kernels
 constexpr int64_t kStripRows = MCCB_STRIP_ROWS;
-// A strip is at most kStripRows rows rounded up to a whole round; the fused kernel's mask
-// staging is unrolled for strips of up to kPlanMaxStripRows rows.
-static_assert(kStripRows + kPlanRound - 1 <= kPlanMaxStripRows, "strips longer than the staging");
+static_assert(kStripRows <= kPlanMaxStripRows, "strips longer than the mask staging");
 constexpr int64_t kMinBlocks = MCCB_MIN_BLOCKS;
 constexpr int64_t kMinStripRows = MCCB_MIN_STRIP_ROWS;
 constexpr int64_t kMaxMaskLds = 48 * 1024;  // bytes of LDS for the staged mask, at most
