@@ -53,7 +53,8 @@
 #include "mccb.h"
 
 // Tuning constants (compile-time; every value here gives the same results, except that the lane
-// layout of the fused kernel fixes the order in which gradWeight's fp64 partial sums are formed).
+// layout of the fused kernel and the strip plan fix the order in which gradWeight's fp64 partial
+// sums are formed).
 // The wide layout of the fused kernel: MCCB_WIDE_VEC columns per lane, MCCB_WIDE_COL_GROUPS
 // column groups MCCB_GROUP_SPACING bytes apart with MCCB_WIDE_RING waves each. The ring layout
 // is fixed: 2 columns per lane, 4 adjacent column groups (2 where registers run short) of 2 waves.

@@ -12,6 +12,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import masked_depthwise_causal_amd as mdc
@@ -176,6 +177,30 @@ def test_plan_is_pure_and_consistent():
         # the plan does not depend on the dtype
         other = FP16 if dt == BF16 else BF16
         assert mdc.mccb_get_plan(S, B, H, other) == p1
+
+
+# Strips of the fused kernel are at most this many rows: the plan aims for strips of 1024 rows and
+# the kernel's mask staging is sized for that bound (a whole number of 16-row rounds).
+MAX_STRIP_ROWS = 1024
+
+
+def test_plan_strip_bounds_over_many_shapes():
+    rng = np.random.default_rng(11)
+    shapes = [(S, B, 384) for S in (1, 2, 15, 16, 17, 127, 128, 129, 1023, 1024, 1025, 1040, 2047,
+                                    2048, 2049, 4095, 4096, 4097, 16383, 16384) for B in (1, 32)]
+    shapes += [(262144, 2, 24576), (524288, 1, 384), (16384, 32, 24576)]
+    for _ in range(200):
+        B = int(rng.integers(1, 33))
+        S = int(rng.integers(1, 524288 // B + 1))
+        shapes.append((S, B, 64 * int(rng.integers(6, 385))))
+    for S, B, H in shapes:
+        p = mdc.mccb_get_plan(S, B, H, BF16)
+        T = p["rows_per_strip"]
+        assert 1 <= T <= MAX_STRIP_ROWS, (S, B, H, T)
+        assert T % 16 == 0 or T >= S, (S, B, H, T)
+        assert p["n_strips"] == -(-S // T)
+        # no more strips than 128-row strips would make (the floor on strip length)
+        assert p["n_strips"] <= max(1, -(-S // 128)), (S, B, H, T)
 
 
 def test_workspace_stays_small_at_the_headline_shape():
