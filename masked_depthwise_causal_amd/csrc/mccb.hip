@@ -110,7 +110,7 @@
 #define MCCB_FWD_VEC 8  // forward: channels per lane (8 = 16-byte loads)
 #endif
 #ifndef MCCB_FWD_WAVES
-#define MCCB_FWD_WAVES 8  // forward: wavefronts per block, side by side across the columns
+#define MCCB_FWD_WAVES 4  // forward: wavefronts per block, side by side across the columns
 #endif
 #ifndef MCCB_FWD_ROWS
 #define MCCB_FWD_ROWS 8  // forward: rows one block covers
@@ -741,7 +741,7 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
 // the page). Pure streaming: read x, write y, nothing to reduce.
 //
 // A block covers a short tile of contiguous columns (kFwdWaves wavefronts, kFwdVec channels per
-// lane; 8 rows x 4096 columns when B*H is large, see `cw` below). Tiles are numbered row-major,
+// lane; 8 rows x 2048 columns when B*H is large, see `cw` below). Tiles are numbered row-major,
 // column tile fastest, so the blocks in flight at any moment sit on a few neighbouring
 // rows; the HBM serves such a compact front markedly faster than many independent column walks.
 // The W-1 rows before the tile are re-read with cached loads (the tile above loaded them, also

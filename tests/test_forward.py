@@ -100,7 +100,7 @@ def test_small_workload_full():
 
 EDGE = [
     # (S, B, H, dtype, mask): S around the row tile, B*H below, at and past the column tile
-    # (4096 columns by default), every mask kind
+    # (2048 columns by default), every mask kind
     (1, 2, 384, "bf16", ("bernoulli", 0.8)),
     (2, 1, 384, "fp16", ("null",)),
     (3, 3, 448, "bf16", ("prefix",)),
