@@ -61,6 +61,9 @@
 #ifndef MCCB_WIDE_VEC
 #define MCCB_WIDE_VEC 4  // columns per lane: 4 -> 8-byte loads
 #endif
+#ifndef MCCB_RING_COL_GROUPS
+#define MCCB_RING_COL_GROUPS 4  // column groups of a ring block (2 where registers run short)
+#endif
 #ifndef MCCB_WIDE_COL_GROUPS
 #define MCCB_WIDE_COL_GROUPS 4
 #endif
@@ -158,7 +161,7 @@ template <int W, bool STRIDED, bool WIDE>
 struct FusedCfg {
     static constexpr bool tight = (STRIDED && W >= 3) || W > 3;
     static constexpr int V = WIDE ? MCCB_WIDE_VEC : 2;  // columns per lane
-    static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS : (tight ? 2 : 4);
+    static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS : (tight ? 2 : MCCB_RING_COL_GROUPS);
     static constexpr int RG = WIDE ? MCCB_WIDE_RING : 2;  // waves per column group
     static constexpr int WPS = WIDE ? MCCB_WIDE_WAVES_PER_SIMD : (tight ? 3 : 4);
     static constexpr int GC = kWave * V;       // columns of one column group
@@ -169,7 +172,7 @@ struct FusedCfg {
     static_assert(!WIDE || W <= 3, "the wide layout holds at most 3 taps of fp64 state");
     static_assert(V == 2 || V == 4, "lane vector must be 4 or 8 bytes");
     static_assert(GC < 384, "a column group spans at most 2 batches (H >= 384)");
-    static_assert(CG <= 4, "the staged mask holds two batches for each of at most 4 groups");
+    static_assert(CG <= 8, "the staged mask holds two batches for each of at most 8 groups");
     static_assert(kPlanRound % RR == 0, "strips must be whole rounds");
     static_assert(BW * kWave <= 1024, "block too large");
     static_assert(DLV % kWave == 0, "group spacing must be a whole number of wave-wide loads");
@@ -189,7 +192,8 @@ constexpr int64_t kPlanBlockCols = 512;
 // Columns of the widest column group (one wave-wide load) of the fused kernel.
 constexpr int64_t kMaxGroupCols = (int64_t)kWave * (MCCB_WIDE_VEC > 2 ? MCCB_WIDE_VEC : 2);
 // Staged mask batches per block: two per column group (a group's columns span at most two).
-constexpr int kMaxStagedBatches = 2 * (MCCB_WIDE_COL_GROUPS > 4 ? MCCB_WIDE_COL_GROUPS : 4);
+constexpr int kMaxStagedBatches =
+    2 * (MCCB_WIDE_COL_GROUPS > MCCB_RING_COL_GROUPS ? MCCB_WIDE_COL_GROUPS : MCCB_RING_COL_GROUPS);
 
 // ---------------------------------------------------------------------------------------------
 // 16-bit formats
