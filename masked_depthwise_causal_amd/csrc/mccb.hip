@@ -157,11 +157,14 @@ struct Vec {
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
 //        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
 //        4-tap windows).
-template <int W, bool STRIDED, bool WIDE>
+constexpr int kLayoutRing = 0, kLayoutWide = 1, kLayoutNarrowRing = 2;
+template <int W, bool STRIDED, int LAYOUT>
 struct FusedCfg {
+    static constexpr bool WIDE = LAYOUT == kLayoutWide;
     static constexpr bool tight = (STRIDED && W >= 3) || W > 3;
     static constexpr int V = WIDE ? MCCB_WIDE_VEC : 2;  // columns per lane
-    static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS : (tight ? 2 : MCCB_RING_COL_GROUPS);
+    static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS
+                                   : ((tight || LAYOUT == kLayoutNarrowRing) ? 2 : MCCB_RING_COL_GROUPS);
     static constexpr int RG = WIDE ? MCCB_WIDE_RING : 2;  // waves per column group
     static constexpr int WPS = WIDE ? MCCB_WIDE_WAVES_PER_SIMD : (tight ? 3 : 4);
     static constexpr int GC = kWave * V;       // columns of one column group
@@ -365,15 +368,15 @@ __device__ static inline int64_t group_first_vec(int64_t cb, int g, int64_t n_sp
 
 // VARLEN (packed variable-length layout, B = 1): `ahead[i]` holds the number of rows i, i+1, ...
 // that belong to row i's sequence (at least 1); the stencil of row i uses only those.
-template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN, bool WIDE>
-__global__ void __launch_bounds__((FusedCfg<W, STRIDED, WIDE>::BW * kWave))
-    __attribute__((amdgpu_waves_per_eu((FusedCfg<W, STRIDED, WIDE>::WPS))))
+template <int DT, bool HAS_MASK, bool STRIDED, int W, bool VARLEN, int LAYOUT>
+__global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
+    __attribute__((amdgpu_waves_per_eu((FusedCfg<W, STRIDED, LAYOUT>::WPS))))
     mccb_fused_bwd(const void *__restrict__ gy_, const void *__restrict__ x_,
                    const void *__restrict__ w_, const uint8_t *__restrict__ mask,
                    void *__restrict__ gx_, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
                    int64_t rows_per_strip, int64_t n_col_blocks, int64_t n_sp_blocks,
                    InStrides st, const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
-    typedef FusedCfg<W, STRIDED, WIDE> Cfg;
+    typedef FusedCfg<W, STRIDED, LAYOUT> Cfg;
     constexpr int V = Cfg::V, CG = Cfg::CG, RG = Cfg::RG, TR = kTurnRows, RR = Cfg::RR;
     typedef typename Vec<V>::t vec_t;
     constexpr int L = W - 1;  // look-ahead rows
@@ -1103,9 +1106,9 @@ struct Profile {
 struct FusedGrid {
     int64_t ncb, n_sp;
 };
-template <int W, bool STRIDED, bool WIDE>
+template <int W, bool STRIDED, int LAYOUT>
 FusedGrid fused_grid(int64_t C) {
-    typedef FusedCfg<W, STRIDED, WIDE> Cfg;
+    typedef FusedCfg<W, STRIDED, LAYOUT> Cfg;
     const int64_t CV = C / Cfg::V;
     FusedGrid g;
     g.n_sp = Cfg::DLV > 0 ? CV / (Cfg::CG * Cfg::DLV) * (Cfg::DLV / kWave) : 0;
@@ -1118,40 +1121,58 @@ FusedGrid fused_grid(int64_t C) {
 // is a whole number of its super-chunks (CG groups x the group spacing); elsewhere the ring layout.
 // A function of the shape only, so gradWeight's summation order is too.
 bool fused_wide(int64_t C, int64_t W) {
-    typedef FusedCfg<3, false, true> Cfg;
+    typedef FusedCfg<3, false, kLayoutWide> Cfg;
     return W <= 3 && Cfg::DLV > 0 && (C / Cfg::V) % (Cfg::CG * Cfg::DLV) == 0;
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).
 int fused_vec(int64_t C, int64_t W) {
-    return fused_wide(C, W) ? FusedCfg<3, false, true>::V : FusedCfg<3, false, false>::V;
+    return fused_wide(C, W) ? FusedCfg<3, false, kLayoutWide>::V : FusedCfg<3, false, kLayoutRing>::V;
 }
 
-template <int DT, bool M, bool T, int TAPS, bool VL, bool WD>
+// The layout a fused launch takes: wide (above), else the ring; the narrow ring (2 column groups
+// instead of 4, so twice the blocks) when the ring's grid would stay under the plan's block target
+// (the 128-row floor on strips stopped the plan short of it), and the ring is not already narrow
+// (strided 3-tap, 4-tap). The column groups of a block do not enter any column's summation
+// order, so the narrow ring's results equal the ring's bit for bit.
+int fused_layout(const Plan &p, bool strided, bool varlen) {
+    if (!varlen && fused_wide(p.C, p.W)) return kLayoutWide;
+    const bool tight = (strided && p.W >= 3) || p.W > 3;
+    if (!tight && fused_grid<3, false, kLayoutRing>(p.C).ncb * p.n_strips < kMinBlocks)
+        return kLayoutNarrowRing;
+    return kLayoutRing;
+}
+
+template <int DT, bool M, bool T, int TAPS, bool VL, int LAYOUT>
 hipError_t launch_fused(const Plan &p, const void *gy, const void *x, const void *w,
                         const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
                         const InStrides &is, const uint8_t *ahead, int lim_lds) {
-    const FusedGrid fg = fused_grid<TAPS, T, WD>(p.C);
-    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS, VL, WD>),
+    const FusedGrid fg = fused_grid<TAPS, T, LAYOUT>(p.C);
+    hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS, VL, LAYOUT>),
                        dim3((unsigned)(fg.ncb * p.n_strips)),
-                       dim3(FusedCfg<TAPS, T, WD>::BW * kWave), lds, st, gy, x, w, mask, gx,
+                       dim3(FusedCfg<TAPS, T, LAYOUT>::BW * kWave), lds, st, gy, x, w, mask, gx,
                        (double *)ws, p.S, p.B, p.H, p.rows_per_strip, fg.ncb, fg.n_sp, is, ahead,
                        lim_lds);
     return hipGetLastError();
 }
 
 template <int DT, bool M, bool T, int TAPS, bool VL>
-hipError_t launch_fused_layout(bool wide, const Plan &p, const void *gy, const void *x,
+hipError_t launch_fused_layout(int layout, const Plan &p, const void *gy, const void *x,
                                const void *w, const uint8_t *mask, void *gx, void *ws,
                                hipStream_t st, size_t lds, const InStrides &is,
                                const uint8_t *ahead, int lim_lds) {
     if constexpr (TAPS <= 3 && !VL) {
-        if (wide)
-            return launch_fused<DT, M, T, TAPS, VL, true>(p, gy, x, w, mask, gx, ws, st, lds, is,
-                                                          ahead, lim_lds);
+        if (layout == kLayoutWide)
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutWide>(p, gy, x, w, mask, gx, ws, st,
+                                                                 lds, is, ahead, lim_lds);
     }
-    return launch_fused<DT, M, T, TAPS, VL, false>(p, gy, x, w, mask, gx, ws, st, lds, is, ahead,
-                                                   lim_lds);
+    if constexpr (!((T && TAPS >= 3) || TAPS > 3)) {  // instantiated where the ring is not narrow
+        if (layout == kLayoutNarrowRing)
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutNarrowRing>(p, gy, x, w, mask, gx, ws,
+                                                                       st, lds, is, ahead, lim_lds);
+    }
+    return launch_fused<DT, M, T, TAPS, VL, kLayoutRing>(p, gy, x, w, mask, gx, ws, st, lds, is,
+                                                         ahead, lim_lds);
 }
 
 // One fused launch for any (mask, strided, W) of the padded layouts (VL false) or the packed one.
@@ -1160,9 +1181,9 @@ hipError_t launch_fused_any(const Plan &p, const void *gy, const void *x, const 
                             const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
                             const InStrides &is, bool strided, const uint8_t *ahead = nullptr,
                             int lim_lds = 0) {
-    const bool wide = !VL && fused_wide(p.C, p.W);
+    const int layout = fused_layout(p, strided, VL);
 #define MCCB_FUSED(M, T, TAPS)                                                                    \
-    return launch_fused_layout<DT, M, T, TAPS, VL>(wide, p, gy, x, w, mask, gx, ws, st, lds, is,  \
+    return launch_fused_layout<DT, M, T, TAPS, VL>(layout, p, gy, x, w, mask, gx, ws, st, lds, is, \
                                                    ahead, lim_lds)
 #define MCCB_FUSED_W(TAPS)                                                                        \
     if constexpr (!VL) {                                                                          \
@@ -1481,16 +1502,29 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     const int rc = check_shape(S, B, H, dtype);
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype);
-    const bool wide = fused_wide(p.C, 3);
-    typedef FusedCfg<3, false, true> Wd;
-    typedef FusedCfg<3, false, false> Rg;
+    const int layout = fused_layout(p, false, false);  // the contiguous 3-tap launch
+    typedef FusedCfg<3, false, kLayoutWide> Wd;
+    typedef FusedCfg<3, false, kLayoutRing> Rg;
+    typedef FusedCfg<3, false, kLayoutNarrowRing> Nr;
     plan->rows_per_turn = kTurnRows;
-    plan->rows_per_round = wide ? Wd::RR : Rg::RR;
     plan->rows_per_strip = p.rows_per_strip;
     plan->n_strips = p.n_strips;
-    plan->cols_per_block = wide ? Wd::CG * Wd::GC : Rg::CG * Rg::GC;
-    plan->n_col_blocks = wide ? fused_grid<3, false, true>(p.C).ncb : fused_grid<3, false, false>(p.C).ncb;
-    plan->waves_per_block = wide ? Wd::BW : Rg::BW;
+    if (layout == kLayoutWide) {
+        plan->rows_per_round = Wd::RR;
+        plan->cols_per_block = Wd::CG * Wd::GC;
+        plan->n_col_blocks = fused_grid<3, false, kLayoutWide>(p.C).ncb;
+        plan->waves_per_block = Wd::BW;
+    } else if (layout == kLayoutNarrowRing) {
+        plan->rows_per_round = Nr::RR;
+        plan->cols_per_block = Nr::CG * Nr::GC;
+        plan->n_col_blocks = fused_grid<3, false, kLayoutNarrowRing>(p.C).ncb;
+        plan->waves_per_block = Nr::BW;
+    } else {
+        plan->rows_per_round = Rg::RR;
+        plan->cols_per_block = Rg::CG * Rg::GC;
+        plan->n_col_blocks = fused_grid<3, false, kLayoutRing>(p.C).ncb;
+        plan->waves_per_block = Rg::BW;
+    }
     plan->workspace_size = p.ws_bytes;
     const FwdPlan f = make_fwd_plan(S, B, H);
     plan->fwd_rows_per_tile = f.rows;
