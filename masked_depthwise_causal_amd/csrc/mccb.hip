@@ -22,7 +22,8 @@
 //     block placed 16 KiB apart in the row, one wave per group. Four wave-wide loads that far apart
 //     are served faster by the HBM than four adjacent ones.
 //   ring (everything else): 4-byte lanes, column groups of adjacent columns with 2 waves each,
-//     which take the strip's rows round robin.
+//     which take the strip's rows round robin; 4 groups per block, or 2 (the narrow ring) where
+//     the plan's grid would otherwise stay small (a column's sums do not depend on the count).
 // Either way a wave takes kTurnRows rows per round, and the block's waves pass a barrier each
 // round, so the block's loads of a row reach the HBM together; each row of gradY, x and gradX
 // crosses HBM once. A wave forms gradX for its kTurnRows rows from the masked gradY rows
