@@ -224,18 +224,22 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
         _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
             raise ValueError("mask must be bool or uint8")
-    if gradX is None:
-        gradX = torch.empty((S, B, H), dtype=dt, device=dev)
-    if gradWeight is None:
-        gradWeight = torch.empty((W, H), dtype=dt, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    # Buffers this call allocates belong to the stream the kernels run on, so that torch's caching
+    # allocator does not hand them to other work before those kernels finish.
+    with torch.cuda.stream(st):
+        if gradX is None:
+            gradX = torch.empty((S, B, H), dtype=dt, device=dev)
+        if gradWeight is None:
+            gradWeight = torch.empty((W, H), dtype=dt, device=dev)
     _check_tensor("gradX", gradX, (S, B, H), dt, dev)
     _check_tensor("gradWeight", gradWeight, (W, H), dt, dev)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
     strides = _strides(gradY, x, weight, mask)
     mptr = None if mask is None else mask.data_ptr()
     if strides is None and W == 3:
         if workspace is None:
-            workspace = workspace_for(S, B, H, dt, dev)
+            with torch.cuda.stream(st):
+                workspace = workspace_for(S, B, H, dt, dev)
         rc = mccb_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
                            gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt],
                            workspace.data_ptr(), _ws_bytes(workspace, dev), st.cuda_stream)
@@ -244,7 +248,8 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
         if workspace is None:
             n = mccb_get_workspace_size_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), S, B,
                                            H, W, DTYPE_CODE[dt], strides)
-            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            with torch.cuda.stream(st):
+                workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         rc = mccb_backward_ex(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(), mptr,
                               gradX.data_ptr(), gradWeight.data_ptr(), S, B, H, W, DTYPE_CODE[dt],
                               strides, workspace.data_ptr(), _ws_bytes(workspace, dev),
@@ -277,10 +282,11 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
         _check_tensor("mask", mask, (B, S), None, dev, contiguous=False)
         if mask.dtype not in (torch.bool, torch.uint8):
             raise ValueError("mask must be bool or uint8")
-    if y is None:
-        y = torch.empty((S, B, H), dtype=dt, device=dev)
-    _check_tensor("y", y, (S, B, H), dt, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
+    if y is None:
+        with torch.cuda.stream(st):  # allocated for the stream the kernel runs on
+            y = torch.empty((S, B, H), dtype=dt, device=dev)
+    _check_tensor("y", y, (S, B, H), dt, dev)
     strides = _strides(None, x, weight, mask)
     mptr = None if mask is None else mask.data_ptr()
     if strides is None and W == 3:
@@ -291,7 +297,8 @@ def forward(x: torch.Tensor, weight: torch.Tensor, mask: torch.Tensor | None = N
         if workspace is None:
             n = mccb_forward_get_workspace_size_ex(x.data_ptr(), weight.data_ptr(), S, B, H, W,
                                                    DTYPE_CODE[dt], strides)
-            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            with torch.cuda.stream(st):
+                workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         rc = mccb_forward_ex(x.data_ptr(), weight.data_ptr(), mptr, y.data_ptr(), S, B, H, W,
                              DTYPE_CODE[dt], strides, workspace.data_ptr(),
                              _ws_bytes(workspace, dev), st.cuda_stream)
@@ -333,16 +340,17 @@ def varlen_backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
     synchronizing."""
     T, H, W, nseq, dev, dt = _varlen_args(x, weight, cu_seqlens, mask)
     _check_tensor("gradY", gradY, (T, H), dt, dev)
-    if gradX is None:
-        gradX = torch.empty((T, H), dtype=dt, device=dev)
-    if gradWeight is None:
-        gradWeight = torch.empty((W, H), dtype=dt, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(st):  # what this call allocates belongs to the kernels' stream
+        if gradX is None:
+            gradX = torch.empty((T, H), dtype=dt, device=dev)
+        if gradWeight is None:
+            gradWeight = torch.empty((W, H), dtype=dt, device=dev)
+        if workspace is None:
+            n = mccb_varlen_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     _check_tensor("gradX", gradX, (T, H), dt, dev)
     _check_tensor("gradWeight", gradWeight, (W, H), dt, dev)
-    if workspace is None:
-        n = mccb_varlen_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    st = stream if stream is not None else torch.cuda.current_stream(dev)
     rc = mccb_varlen_backward(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
                               None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
                               gradX.data_ptr(), gradWeight.data_ptr(), T, nseq, H, W,
@@ -360,13 +368,14 @@ def varlen_forward(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tens
     """Packed variable-length layout: y [T,H] = mask * causal depthwise conv(x, weight) within
     each sequence. Enqueues without synchronizing."""
     T, H, W, nseq, dev, dt = _varlen_args(x, weight, cu_seqlens, mask)
-    if y is None:
-        y = torch.empty((T, H), dtype=dt, device=dev)
-    _check_tensor("y", y, (T, H), dt, dev)
-    if workspace is None:
-        n = mccb_varlen_forward_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(st):  # what this call allocates belongs to the kernel's stream
+        if y is None:
+            y = torch.empty((T, H), dtype=dt, device=dev)
+        if workspace is None:
+            n = mccb_varlen_forward_get_workspace_size(T, nseq, H, W, DTYPE_CODE[dt])
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("y", y, (T, H), dt, dev)
     rc = mccb_varlen_forward(x.data_ptr(), weight.data_ptr(),
                              None if mask is None else mask.data_ptr(), cu_seqlens.data_ptr(),
                              y.data_ptr(), T, nseq, H, W, DTYPE_CODE[dt], workspace.data_ptr(),
