@@ -62,6 +62,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_backward_w.restype = ctypes.c_int
     lib.oracle_forward_w.argtypes = [ctypes.c_int, i64, i64, i64, _f64p, _f64p, _u8p, _f64p]
     lib.oracle_forward_w.restype = ctypes.c_int
+    lib.oracle_backward_rows_w.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64,
+                                           _u16p, _u16p, _u16p, _u8p, _u16p, _f64p, _f64p]
+    lib.oracle_backward_rows_w.restype = ctypes.c_int
     _i64p = ctypes.POINTER(ctypes.c_int64)
     lib.oracle_backward_varlen.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, _i64p, _u16p,
                                            _u16p, _u16p, _u8p, _f64p, _u16p, _f64p, _f64p, _u16p]
@@ -146,6 +149,39 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle_backward failed ({rc})")
         return out
+
+    def backward_rows(self, dtype: str, S: int, r0: int, r1: int, gY_rows: np.ndarray,
+                      x_rows: np.ndarray, w: np.ndarray, mask: np.ndarray | None,
+                      gw_acc: np.ndarray, gw_sq: np.ndarray | None = None) -> np.ndarray:
+        """Rows r0 .. r1-1 of a problem with S rows: returns gradX of those rows (uint16
+        [r1-r0,B,H]) and adds their gradWeight terms (and squared terms) into the float64 [W,H]
+        arrays gw_acc (and gw_sq). gY_rows holds gradY rows r0 .. min(r1+W-1, S)-1, x_rows x rows
+        r0 .. r1-1, mask is the whole [B,S] mask or None."""
+        gY_rows = np.ascontiguousarray(gY_rows, dtype=np.uint16)
+        x_rows = np.ascontiguousarray(x_rows, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        W = int(w.shape[0])
+        n, B, H = x_rows.shape
+        if n != r1 - r0 or gY_rows.shape != (min(r1 + W - 1, S) - r0, B, H):
+            raise ValueError("row slabs do not match r0, r1, S and W")
+        if gw_acc.dtype != np.float64 or gw_acc.shape != (W, H) or not gw_acc.flags.c_contiguous:
+            raise ValueError("gw_acc must be a contiguous float64 [W,H] array")
+        if gw_sq is not None and (gw_sq.dtype != np.float64 or gw_sq.shape != (W, H) or
+                                  not gw_sq.flags.c_contiguous):
+            raise ValueError("gw_sq must be a contiguous float64 [W,H] array")
+        m = None
+        if mask is not None:
+            m = np.ascontiguousarray(mask).astype(np.uint8, copy=False)
+            if m.shape != (B, S):
+                raise ValueError("mask must be the whole [B,S] mask")
+        gx16 = np.empty((n, B, H), dtype=np.uint16)
+        rc = self.lib.oracle_backward_rows_w(
+            DTYPE_CODE[dtype], W, S, B, H, r0, r1, _ptr(gY_rows, _u16p), _ptr(x_rows, _u16p),
+            _ptr(w, _u16p), None if m is None else _ptr(m, _u8p), _ptr(gx16, _u16p),
+            _ptr(gw_acc, _f64p), None if gw_sq is None else _ptr(gw_sq, _f64p))
+        if rc != 0:
+            raise RuntimeError(f"oracle_backward_rows_w failed ({rc})")
+        return gx16
 
     def forward(self, x64: np.ndarray, w64: np.ndarray, mask: np.ndarray | None) -> np.ndarray:
         """fp64 causal depthwise forward y = mask * conv(x, w), w [W,H]; used by the adjoint test

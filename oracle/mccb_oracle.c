@@ -218,6 +218,73 @@ int oracle_backward_w(int dtype, int W, int64_t S, int64_t B, int64_t H, const u
     return 0;
 }
 
+/*
+ * The same three equations over a range of rows, for tensors too large to hold whole on the host:
+ * gradX rows r0 .. r1-1, and the gradWeight terms of those rows (gradX rows i in [r0, r1) in the
+ * gradWeight equation) added into caller-held fp64 sums. Running it over consecutive ranges that
+ * cover 0 .. S-1 gives every gradX row and the whole gradWeight sum (summed range by range; within
+ * a range j outer, i inner, as above).
+ *   gY_rows: [n_gy, B, H] 16-bit patterns of gradY rows r0 .. r0+n_gy-1, where
+ *            n_gy = min(r1 + W - 1, S) - r0 (the range and the W-1 rows after it, up to S)
+ *   x_rows : [r1 - r0, B, H] rows r0 .. r1-1 of x
+ *   w      : [W, H]; mask: the whole [B,S] mask, or NULL
+ *   gx16   : [r1 - r0, B, H] gradX rows r0 .. r1-1 rounded to dtype (may be NULL)
+ *   gw_acc, gw_sq: [W, H] fp64, incremented by the terms and by their squares (either may be NULL)
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_backward_rows_w(int dtype, int W, int64_t S, int64_t B, int64_t H, int64_t r0,
+                           int64_t r1, const uint16_t *gY_rows, const uint16_t *x_rows,
+                           const uint16_t *w, const uint8_t *mask, uint16_t *gx16, double *gw_acc,
+                           double *gw_sq) {
+    if (S < 1 || B < 1 || H < 1 || W < 1 || !gY_rows || !x_rows || !w) return -1;
+    if (dtype != OR_BF16 && dtype != OR_FP16) return -1;
+    if (r0 < 0 || r1 <= r0 || r1 > S) return -1;
+    const int64_t n_gy = (r1 + W - 1 < S ? r1 + W - 1 : S) - r0, n_x = r1 - r0;
+    double *gyd = (double *)malloc(sizeof(double) * (size_t)(n_gy * B * H));
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(n_x * B * H));
+    double *wd = (double *)malloc(sizeof(double) * (size_t)(W * H));
+    if (!gyd || !xd || !wd) {
+        free(gyd);
+        free(xd);
+        free(wd);
+        return -1;
+    }
+    oracle_decode(dtype, gY_rows, gyd, n_gy * B * H);
+    oracle_decode(dtype, x_rows, xd, n_x * B * H);
+    oracle_decode(dtype, w, wd, (int64_t)W * H);
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < H; ++h) {
+        /* gradYMasked of absolute row i, batch j (zero for i >= S); row i sits at i - r0 */
+#define GYM(i, j) ((i) >= S ? 0.0                                                           \
+                   : ((mask == NULL || mask[(j) * S + (i)] != 0) ? 1.0 : 0.0) *            \
+                         gyd[(((i) - r0) * B + (j)) * H + h])
+        for (int64_t i = r0; i < r1; ++i) {
+            for (int64_t j = 0; j < B; ++j) {
+                double acc = 0.0;
+                for (int k = 0; k < W; ++k) acc += GYM(i + k, j) * wd[(W - 1 - k) * H + h];
+                if (gx16) gx16[((i - r0) * B + j) * H + h] = encode_one(dtype, acc);
+            }
+        }
+        for (int k = 0; k < W; ++k) {
+            double acc = 0.0, sq = 0.0;
+            for (int64_t j = 0; j < B; ++j) {
+                for (int64_t i = r0; i < r1; ++i) {
+                    const double term = GYM(i + W - 1 - k, j) * xd[((i - r0) * B + j) * H + h];
+                    acc += term;
+                    sq += term * term;
+                }
+            }
+            if (gw_acc) gw_acc[k * H + h] += acc;
+            if (gw_sq) gw_sq[k * H + h] += sq;
+        }
+#undef GYM
+    }
+    free(gyd);
+    free(xd);
+    free(wd);
+    return 0;
+}
+
 /* The page's window, W = 3. */
 int oracle_backward(int dtype, int64_t S, int64_t B, int64_t H, const uint16_t *gY,
                     const uint16_t *x, const uint16_t *w, const uint8_t *mask, double *gx64,

@@ -406,7 +406,53 @@ def pin_codec_encode_bf16(orc):
     assert np.all(same | zero)
 
 
-PINS = [pin_hand_cases, pin_forward_hand_cases, pin_window_hand_cases,
+def _rows_run(orc, dtype, gy, x, w, m, cuts):
+    """The row-range oracle over consecutive ranges split at `cuts`: (gradX bits, fp64 sums, sums
+    of squared terms)."""
+    S, B, H = gy.shape
+    W = w.shape[0]
+    acc = np.zeros((W, H)), np.zeros((W, H))
+    parts = []
+    edges = [0, *cuts, S]
+    for r0, r1 in zip(edges[:-1], edges[1:]):
+        parts.append(orc.backward_rows(dtype, S, r0, r1, gy[r0:min(r1 + W - 1, S)], x[r0:r1], w, m,
+                                       acc[0], acc[1]))
+    return np.concatenate(parts), acc[0], acc[1]
+
+
+def pin_rows_hand_cases(orc):
+    """The row-range entry point on the hand-worked cases, one row per range: every gradX value and
+    the gradWeight sums are the derived ones."""
+    for c in json.load(open(GOLDEN))["cases"]:
+        for dtype in ("bf16", "fp16"):
+            gy, x, w = to_bits(c["gY"], dtype), to_bits(c["x"], dtype), to_bits(c["w"], dtype)
+            m = None if c["mask"] is None else np.array(c["mask"], dtype=np.uint8)
+            gx16, gw, sq = _rows_run(orc, dtype, gy, x, w, m, list(range(1, gy.shape[0])))
+            tag = f"{c['name']}/{dtype}"
+            assert np.array_equal(from_bits(gx16, dtype), np.array(c["gX"], float)), tag
+            assert np.array_equal(gw, np.array(c["gW"], float)), tag
+            assert np.array_equal(sq, np.array(c["gW_sumsq"], float)), tag
+
+
+def pin_rows_equal_whole(orc):
+    """Consecutive row ranges (of every length from 1, ending anywhere, with and without a mask,
+    1-4 taps) give the whole-tensor oracle's gradX bit for bit and its gradWeight sums up to fp64
+    reordering (the whole-tensor oracle is pinned independently above)."""
+    for W in (1, 2, 3, 4):
+        for mask in (("bernoulli", 0.7), ("null",)):
+            gy, x, w, m = random_case(23, 3, 24, "bf16", mask, seed=30 + W)
+            w = to_bits(np.resize(from_bits(w, "bf16"), (W, 24)), "bf16")
+            whole = orc.backward("bf16", gy, x, w, m)
+            for cuts in ([], [1], [22], [5, 6, 7, 20], list(range(1, 23)), [3, 11, 21]):
+                gx16, gw, sq = _rows_run(orc, "bf16", gy, x, w, m, cuts)
+                tag = (W, mask[0], cuts)
+                assert np.array_equal(gx16, whole["gx16"]), tag
+                scale = np.maximum(whole["gwrss"], 1e-300)
+                assert np.all(np.abs(gw - whole["gw64"]) <= 1e-12 * scale), tag
+                np.testing.assert_allclose(np.sqrt(sq), whole["gwrss"], rtol=1e-12, err_msg=str(tag))
+
+
+PINS = [pin_hand_cases, pin_rows_hand_cases, pin_rows_equal_whole, pin_forward_hand_cases, pin_window_hand_cases,
         pin_window_autograd_and_adjoint, pin_varlen_hand_cases, pin_varlen_equals_padded,
         pin_call_example, pin_autograd, pin_adjoint, pin_forward, pin_invariants,
         pin_codec_decode, pin_codec_roundtrip, pin_codec_encode_fp16, pin_codec_encode_bf16]
@@ -502,6 +548,12 @@ MUTANTS = [
     ("varlen forward ignores the token mask",
      "mask[t] != 0) ? 1.0 : 0.0;\n                y[t * H + h] = m * acc;",
      "mask[t] != 0) ? 1.0 : 1.0;\n                y[t * H + h] = m * acc;"),
+    ("row ranges cut the window at the range end", "#define GYM(i, j) ((i) >= S ? 0.0",
+     "#define GYM(i, j) ((i) >= r1 ? 0.0"),
+    ("row ranges shift the gradWeight tap", "GYM(i + W - 1 - k, j) * xd", "GYM(i + k, j) * xd"),
+    ("row ranges read the mask untransposed", "mask[(j) * S + (i)]", "mask[(i) * B + (j)]"),
+    ("row ranges overwrite the caller's sums", "if (gw_acc) gw_acc[k * H + h] += acc;",
+     "if (gw_acc) gw_acc[k * H + h] = acc;"),
     ("encoder saturates on overflow",
      "if (field >= (double)inf_field) return (uint16_t)(sign | inf_field);",
      "if (field >= (double)inf_field) return (uint16_t)(sign | (inf_field - 1u));"),
