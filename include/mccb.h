@@ -58,7 +58,9 @@ enum {
      * H in [384, 24576] and H % 64 == 0 (constraints section) */
     MCCB_ERR_SHAPE = 561002,
     /* a HIP runtime call or kernel launch failed (the page names no code for this) */
-    MCCB_ERR_RUNTIME = -1
+    MCCB_ERR_RUNTIME = -1,
+    /* mccb_backward_noalloc: the shape needs more workspace than its fixed scratch holds */
+    MCCB_ERR_SCRATCH_LIMIT = -2
 };
 
 /*
@@ -95,6 +97,29 @@ int mccb_get_workspace_size(int64_t S, int64_t B, int64_t H, int dtype, uint64_t
 int mccb_backward(const void *gradY, const void *x, const void *weight, const uint8_t *mask,
                   void *gradX, void *gradWeight, int64_t S, int64_t B, int64_t H, int dtype,
                   void *workspace, uint64_t workspace_size, void *stream);
+
+/*
+ * mccb_backward for callers that cannot allocate device memory: code recorded under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc. Same arguments, results (bit for
+ * bit), validation and error codes as mccb_backward, without the workspace: the gradWeight
+ * partials go to a fixed scratch array of MCCB_NOALLOC_SCRATCH_BYTES that the library's device
+ * code holds on every device it runs on (allocated when the library's code is loaded on that
+ * device, kept until the process ends). This call allocates nothing: no hipMalloc, no hipFree.
+ *
+ * A shape whose workspace (mccb_get_workspace_size) exceeds MCCB_NOALLOC_SCRATCH_BYTES returns
+ * MCCB_ERR_SCRATCH_LIMIT and enqueues nothing (S=16384 B=32 H=5120 needs 62,914,560 bytes and
+ * fits; S=262144 B=2 H=24576 needs 301,989,888 and does not). The scratch needs no clearing: every
+ * call overwrites the part it reads. All calls on one device share that device's scratch, so two
+ * calls that can run at the same time on one device (on different streams, or from different
+ * threads without ordering) race and give wrong gradWeight; calls ordered on one stream do not.
+ * The kernels run on the device of `stream` (NULL = the current device's default stream). The
+ * first call on a device also looks up the scratch address there (hipGetSymbolAddress), so that
+ * call must not itself be under graph capture; MCCB_ERR_RUNTIME if the lookup fails.
+ */
+#define MCCB_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int mccb_backward_noalloc(const void *gradY, const void *x, const void *weight,
+                          const uint8_t *mask, void *gradX, void *gradWeight, int64_t S,
+                          int64_t B, int64_t H, int dtype, void *stream);
 
 /*
  * The forward operation whose gradients mccb_backward computes: the masked causal depthwise

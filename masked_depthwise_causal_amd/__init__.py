@@ -23,6 +23,8 @@ MCCB_ERR_PARAM_NULLPTR = 161001
 MCCB_ERR_PARAM_INVALID = 161002
 MCCB_ERR_SHAPE = 561002
 MCCB_ERR_RUNTIME = -1
+MCCB_ERR_SCRATCH_LIMIT = -2
+MCCB_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed scratch of mccb_backward_noalloc (mccb.h)
 
 DTYPE_CODE = {torch.bfloat16: MCCB_BF16, torch.float16: MCCB_FP16}
 
@@ -50,6 +52,14 @@ def mccb_backward(gradY: int, x: int, weight: int, mask: int | None, gradX: int,
     """Raw call with integer device addresses; returns the status code (does not raise)."""
     return int(lib().mccb_backward(gradY, x, weight, mask, gradX, gradWeight, S, B, H, dtype,
                                    workspace, workspace_size, stream))
+
+
+def mccb_backward_noalloc(gradY: int, x: int, weight: int, mask: int | None, gradX: int,
+                          gradWeight: int, S: int, B: int, H: int, dtype: int,
+                          stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the status code (does not raise)."""
+    return int(lib().mccb_backward_noalloc(gradY, x, weight, mask, gradX, gradWeight, S, B, H,
+                                           dtype, stream))
 
 
 def mccb_forward(x: int, weight: int, mask: int | None, y: int, S: int, B: int, H: int, dtype: int,
@@ -257,6 +267,36 @@ def backward(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
         where = "mccb_backward_ex"
     if rc != MCCB_OK:
         raise MccbError(rc, where)
+    return gradX, gradWeight
+
+
+def backward_noalloc(gradY: torch.Tensor, x: torch.Tensor, weight: torch.Tensor,
+                     mask: torch.Tensor | None, gradX: torch.Tensor, gradWeight: torch.Tensor,
+                     stream: torch.cuda.Stream | None = None):
+    """mccb_backward_noalloc on contiguous device tensors: the caller passes both outputs and no
+    workspace, and nothing is allocated (the library's fixed device scratch holds the gradWeight
+    partials). 3-tap window only. Enqueues on `stream` (default: torch's current stream)."""
+    if gradY.dim() != 3:
+        raise ValueError("gradY must be [S,B,H]")
+    S, B, H = (int(s) for s in gradY.shape)
+    dev, dt = gradY.device, gradY.dtype
+    if dt not in DTYPE_CODE:
+        raise ValueError(f"dtype {dt} not supported (bfloat16, float16)")
+    _check_tensor("gradY", gradY, (S, B, H), dt, dev)
+    _check_tensor("x", x, (S, B, H), dt, dev)
+    _check_tensor("weight", weight, (3, H), dt, dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (B, S), None, dev)
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be bool or uint8")
+    _check_tensor("gradX", gradX, (S, B, H), dt, dev)
+    _check_tensor("gradWeight", gradWeight, (3, H), dt, dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = mccb_backward_noalloc(gradY.data_ptr(), x.data_ptr(), weight.data_ptr(),
+                               None if mask is None else mask.data_ptr(), gradX.data_ptr(),
+                               gradWeight.data_ptr(), S, B, H, DTYPE_CODE[dt], st.cuda_stream)
+    if rc != MCCB_OK:
+        raise MccbError(rc, "mccb_backward_noalloc")
     return gradX, gradWeight
 
 

@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
         L.mccb_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
                                     vp, u64, vp]
         L.mccb_backward.restype = ctypes.c_int
+        L.mccb_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
+                                            vp]
+        L.mccb_backward_noalloc.restype = ctypes.c_int
         L.mccb_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
         L.mccb_forward.restype = ctypes.c_int
         sp = ctypes.POINTER(Strides)

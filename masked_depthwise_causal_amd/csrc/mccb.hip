@@ -123,6 +123,12 @@
 #define MCCB_FWD_LDS 0  // forward: LDS reserved per block to cap blocks per CU (0: no cap)
 #endif
 
+// Fixed device scratch of mccb_backward_noalloc (the fp64 gradWeight partials), in place of a
+// caller's workspace; see scratch_on() below for how host code reaches it.
+constexpr uint64_t kScratchBytes = MCCB_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch holds whole 256-byte lines");
+static __device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1486,6 +1492,85 @@ int check_varlen(int64_t T, int64_t nseq, int64_t H, int64_t W, int dtype) {
     return rc;
 }
 
+// Alignment and overlap checks of the contiguous 3-tap backward (after the entry point's pointer,
+// shape and workspace-size checks). `workspace` may be nullptr when the call brings none.
+int check_contiguous(const Plan &p, const void *gradY, const void *x, const void *weight,
+                     const uint8_t *mask, const void *gradX, const void *gradWeight,
+                     const void *workspace) {
+    const int64_t S = p.S, B = p.B, H = p.H;
+    if (!aligned16(gradY) || !aligned16(x) || !aligned16(weight) || !aligned16(gradX) ||
+        !aligned16(gradWeight) || (workspace && p.ws_bytes > 0 && !aligned16(workspace)))
+        return MCCB_ERR_PARAM_INVALID;
+    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
+    const uint64_t mb = mask ? (uint64_t)(B * S) : 0u;
+    // No output (nor the workspace) may overlap any other buffer; in particular gradX cannot
+    // alias gradY, whose rows the stencil reads ahead of the rows it writes.
+    const void *bufs[7] = {gradY, x, weight, mask, gradX, gradWeight, workspace};
+    const uint64_t lens[7] = {nb, nb, wb, mb, nb, wb, workspace ? p.ws_bytes : 0u};
+    if (any_overlap(bufs, lens, 7, 4)) return MCCB_ERR_PARAM_INVALID;
+    return MCCB_OK;
+}
+
+// Enqueues the two kernels of the contiguous 3-tap backward on `stream`; `workspace` holds at
+// least p.ws_bytes.
+int launch_contiguous(const Plan &p, const void *gradY, const void *x, const void *weight,
+                      const uint8_t *mask, void *gradX, void *gradWeight, void *workspace,
+                      void *stream) {
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t *ev = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.on && g_prof.n < g_prof.cap) ev = &g_prof.ev[3 * (size_t)g_prof.n++];
+    }
+    const InStrides is{p.B * p.H, p.H, p.B * p.H, p.H, p.S, 1};
+    const hipError_t e =
+        (p.dtype == MCCB_BF16)
+            ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
+                                is, false)
+            : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
+                                is, false);
+    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fixed scratch of mccb_backward_noalloc: the gradWeight partials live in `scratch`, a device
+// array of the library's code object (each device the library runs on holds its own copy until
+// the process ends), instead of a caller's workspace. In host code `scratch` names only a host
+// stand-in for the symbol; its device address, which differs per device, comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and only that address
+// reaches a kernel. Every call on one device shares its copy; the fused kernel overwrites every
+// partial the reduction reads, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+struct ScratchTable {
+    std::mutex mu;
+    void *ptr[kMaxDevices] = {};
+} g_scratch;
+
+// Device address of `scratch` on the device that runs `stream` (the current device for the null
+// stream), or nullptr if a HIP call fails.
+void *scratch_on(hipStream_t stream) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch.mu);
+    if (!g_scratch.ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return nullptr;
+        if (e != hipSuccess || !p) return nullptr;
+        g_scratch.ptr[dev] = p;
+    }
+    return g_scratch.ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1544,36 +1629,29 @@ int mccb_backward(const void *gradY, const void *x, const void *weight, const ui
     const Plan p = make_plan(S, B, H, dtype);
     if (p.ws_bytes > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
     if (workspace_size < p.ws_bytes) return MCCB_ERR_PARAM_INVALID;
-    if (!aligned16(gradY) || !aligned16(x) || !aligned16(weight) || !aligned16(gradX) ||
-        !aligned16(gradWeight) || (p.ws_bytes > 0 && !aligned16(workspace)))
-        return MCCB_ERR_PARAM_INVALID;
-    const uint64_t nb = (uint64_t)(S * B * H) * 2u, wb = (uint64_t)(3 * H) * 2u;
-    const uint64_t mb = mask ? (uint64_t)(B * S) : 0u;
-    // No output (nor the workspace) may overlap any other buffer; in particular gradX cannot
-    // alias gradY, whose rows the stencil reads ahead of the rows it writes.
-    const void *bufs[7] = {gradY, x, weight, mask, gradX, gradWeight, workspace};
-    const uint64_t lens[7] = {nb, nb, wb, mb, nb, wb, p.ws_bytes};
-    for (int o = 4; o < 7; ++o) {
-        if (!bufs[o] || lens[o] == 0) continue;
-        for (int t = 0; t < 7; ++t) {
-            if (t == o || !bufs[t] || lens[t] == 0) continue;
-            if (overlaps(bufs[o], lens[o], bufs[t], lens[t])) return MCCB_ERR_PARAM_INVALID;
-        }
-    }
+    const int vr = check_contiguous(p, gradY, x, weight, mask, gradX, gradWeight,
+                                    p.ws_bytes > 0 ? workspace : nullptr);
+    if (vr != MCCB_OK) return vr;
+    return launch_contiguous(p, gradY, x, weight, mask, gradX, gradWeight, workspace, stream);
+}
 
-    hipStream_t st = (hipStream_t)stream;
-    hipEvent_t *ev = nullptr;
-    {
-        std::lock_guard<std::mutex> lk(g_prof.mu);
-        if (g_prof.on && g_prof.n < g_prof.cap) ev = &g_prof.ev[3 * (size_t)g_prof.n++];
+int mccb_backward_noalloc(const void *gradY, const void *x, const void *weight,
+                          const uint8_t *mask, void *gradX, void *gradWeight, int64_t S,
+                          int64_t B, int64_t H, int dtype, void *stream) {
+    if (!gradY || !x || !weight || !gradX || !gradWeight) return MCCB_ERR_PARAM_NULLPTR;
+    const int rc = check_shape(S, B, H, dtype);
+    if (rc != MCCB_OK) return rc;
+    const Plan p = make_plan(S, B, H, dtype);
+    if (p.ws_bytes > kScratchBytes) return MCCB_ERR_SCRATCH_LIMIT;
+    const int vr = check_contiguous(p, gradY, x, weight, mask, gradX, gradWeight, nullptr);
+    if (vr != MCCB_OK) return vr;
+    // validation done: the first HIP call comes here
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        ws = scratch_on((hipStream_t)stream);
+        if (!ws) return MCCB_ERR_RUNTIME;
     }
-    const hipError_t e =
-        (dtype == MCCB_BF16)
-            ? launch<MCCB_BF16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
-                                InStrides{B * H, H, B * H, H, S, 1}, false)
-            : launch<MCCB_FP16>(p, gradY, x, weight, mask, gradX, gradWeight, workspace, st, ev,
-                                InStrides{B * H, H, B * H, H, S, 1}, false);
-    return e == hipSuccess ? MCCB_OK : MCCB_ERR_RUNTIME;
+    return launch_contiguous(p, gradY, x, weight, mask, gradX, gradWeight, ws, stream);
 }
 
 int mccb_forward(const void *x, const void *weight, const uint8_t *mask, void *y, int64_t S,
@@ -1807,6 +1885,9 @@ const char *mccb_status_string(int status) {
             return "MCCB_ERR_PARAM_INVALID: bad dtype, alignment, overlap or workspace size";
         case MCCB_ERR_SHAPE: return "MCCB_ERR_SHAPE: shape outside the supported range";
         case MCCB_ERR_RUNTIME: return "MCCB_ERR_RUNTIME: HIP launch failed";
+        case MCCB_ERR_SCRATCH_LIMIT:
+            return "MCCB_ERR_SCRATCH_LIMIT: the shape needs more than the fixed scratch of "
+                   "mccb_backward_noalloc (call mccb_backward with a workspace)";
         default: return "unknown mccb status";
     }
 }

@@ -123,6 +123,54 @@ def test_overlapping_buffers(case):
     assert call(**case) == INVALID
 
 
+# -- mccb_backward_noalloc: same validation, no workspace, a fixed scratch limit -----------------
+def ncall(gy=GY, x=X, w=W, m=M, gx=GX, gw=GW, S=64, B=2, H=384, dt=BF16, stream=None):
+    rc = mdc.mccb_backward_noalloc(gy, x, w, m, gx, gw, S, B, H, dt, stream)
+    assert rc in VALIDATION_CODES | {mdc.MCCB_ERR_SCRATCH_LIMIT}, \
+        f"no-alloc call passed validation with fake pointers (rc={rc})"
+    return rc
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
+def test_noalloc_null_required_pointer(which):
+    assert ncall(**{which: None}) == NULLPTR
+
+
+@pytest.mark.parametrize("dt", [-1, 2])
+def test_noalloc_bad_dtype(dt):
+    assert ncall(dt=dt) == INVALID
+
+
+@pytest.mark.parametrize("S,B,H", [(64, 0, 384), (64, 2, 320), (16385, 32, 384)])
+def test_noalloc_shape_out_of_range(S, B, H):
+    assert ncall(S=S, B=B, H=H) == SHAPE
+
+
+@pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
+def test_noalloc_misaligned_pointer(which):
+    base = {"gy": GY, "x": X, "w": W, "gx": GX, "gw": GW}[which]
+    assert ncall(**{which: base + 8}) == INVALID
+
+
+@pytest.mark.parametrize("case", [dict(gx=GY), dict(gx=X + 1024), dict(gw=GX + 256),
+                                  dict(gw=W), dict(gx=M - 512)])
+def test_noalloc_overlapping_buffers(case):
+    assert ncall(**case) == INVALID
+
+
+def test_noalloc_scratch_limit():
+    # the headline shape fits the fixed scratch; S=262144 B=2 H=24576 does not and is refused
+    # before anything is enqueued (the limit is checked after the shape, before any HIP call)
+    limit = mdc.MCCB_NOALLOC_SCRATCH_BYTES
+    assert limit == 64 << 20
+    assert re.search(r"#define\s+MCCB_NOALLOC_SCRATCH_BYTES\s+\(64ull << 20\)",
+                     open(HEADER).read())
+    assert _ws(16384, 32, 5120) <= limit
+    assert _ws(262144, 2, 24576) > limit
+    assert ncall(S=262144, B=2, H=24576) == mdc.MCCB_ERR_SCRATCH_LIMIT
+    assert "SCRATCH" in mdc.mccb_status_string(mdc.MCCB_ERR_SCRATCH_LIMIT)
+
+
 Y = GX  # the forward's output slot
 
 
