@@ -3,8 +3,8 @@
 Bars (stated in the tests): gradX within 1 ulp of the oracle's correctly rounded value (and, by
 design, bit-exact); gradWeight within relative error 8e-3 (bf16) / 1e-3 (fp16) of the oracle's exact
 fp64 value (and, by design, equal to its rounding up to 1 ulp). Small shapes are compared element by
-element; the full-size workloads, in the launch configuration the benchmark times, are compared on
-every element of sampled channels and of sampled rows.
+element; the full-size workloads are compared whole in test_full_parity.py, and the longest sequence
+(S=524288, B=1) here on every element of sampled channels and of sampled rows.
 """
 from __future__ import annotations
 
@@ -109,23 +109,6 @@ def test_subnormal_outputs_full():
     for wl in cases:
         gx, gw = gpu_run(wl)
         compare_full(wl, gx, gw, tag=wl.name + " subnormal")
-
-
-@pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=lambda i: WORKLOADS[i].name)
-def test_full_size_workload_sampled(idx):
-    wl = WORKLOADS[idx]
-    inputs = gpu_inputs(wl)
-    gx, gw = gpu_run(wl, inputs)
-    announce(f"compare {wl.name}: sampled channels")
-    compare_columns(wl, gx, gw, sample_channels(wl, seed=idx))
-    announce(f"compare {wl.name}: sampled rows")
-    compare_rows(wl, gx, sample_rows(wl, plan_of(wl), seed=idx))
-    # a second run on the same inputs gives the same bits
-    gx2, gw2 = gpu_run(wl, inputs, poison_workspace=True)
-    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16))
-    assert torch.equal(gw.view(torch.int16), gw2.view(torch.int16))
-    del gx, gw, gx2, gw2, inputs
-    torch.cuda.empty_cache()
 
 
 def test_generator_same_bits_on_gpu_and_cpu():
