@@ -36,6 +36,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(_build.LIB):
+            if os.environ.get("MCCB_LIBRARY"):
+                raise OSError(f"MCCB_LIBRARY={_build.LIB} does not exist")
             _build.build_library()
         L = ctypes.CDLL(_build.LIB)
         i64, u64, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p

@@ -7,7 +7,9 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mccb.hip")
-LIB = os.path.join(PKG, "libmccb.so")
+# MCCB_LIBRARY names another build of the library to load instead (the tests' host-sanitized
+# build); it is loaded as given and never built.
+LIB = os.environ.get("MCCB_LIBRARY") or os.path.join(PKG, "libmccb.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC_FLAGS = [

@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mccb_oracle.c")
-_LIB = os.path.join(_HERE, "libmccb_oracle.so")
+# MCCB_ORACLE_LIBRARY names another build of the oracle to load by default (the tests'
+# sanitized build).
+_LIB = os.environ.get("MCCB_ORACLE_LIBRARY") or os.path.join(_HERE, "libmccb_oracle.so")
 
 DTYPE_CODE = {"bf16": 0, "fp16": 1}
 

@@ -17,14 +17,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 @pytest.fixture(scope="module")
 def client_output(tmp_path_factory):
-    gcc = shutil.which("gcc")
-    if gcc is None:
-        pytest.skip("gcc not available")
+    # MCCB_TEST_CC: another C compiler command line (the sanitized run uses clang with the
+    # address and undefined-behaviour sanitizers)
+    cc = os.environ.get("MCCB_TEST_CC", "gcc").split()
+    if shutil.which(cc[0]) is None:
+        pytest.skip(f"{cc[0]} not available")
     mdc.lib()  # builds the library if it is missing
-    lib_dir = os.path.dirname(build.LIB)
+    lib_dir, lib_name = os.path.split(build.LIB)
     exe = str(tmp_path_factory.mktemp("cabi") / "c_abi_client")
-    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", build.INCLUDE,
-           os.path.join(HERE, "c_abi_client.c"), "-o", exe, "-L", lib_dir, "-l:libmccb.so",
+    cmd = [*cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", build.INCLUDE,
+           os.path.join(HERE, "c_abi_client.c"), "-o", exe, "-L", lib_dir, f"-l:{lib_name}",
            f"-Wl,-rpath,{lib_dir}"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
