@@ -36,8 +36,13 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mccb_fused_bwd_S16384_B32_H5120_bf16_traffic.txt")
-FWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mccb_fwd_S16384_B32_H5120_bf16_traffic.txt")
+def traffic_file(kernel: str, workload_name: str) -> str:
+    """The committed rocprofv3 counter summary of one kernel on one workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_traffic.txt")
+
+
+TRAFFIC_FILE = traffic_file("mccb_fused_bwd", "S16384_B32_H5120_bf16")
+FWD_TRAFFIC_FILE = traffic_file("mccb_fwd", "S16384_B32_H5120_bf16")
 KERNEL_SRC = os.path.join(ROOT, "masked_depthwise_causal_amd", "csrc", "mccb.hip")
 
 
@@ -174,7 +179,17 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
     after reading a 1 GiB scratch buffer so that no input is left in the 256 MB Infinity Cache or
     the L2s (the small workloads would otherwise run from cache). The flush reads rather than
     writes, so no dirty lines are left to be written back during the timed call. Median and
-    minimum."""
+    minimum.
+
+    For the backward a second pass of the same calls records the library's HIP events around its
+    two kernels (mccb_profile_begin/_end): `fused_kernel` is the fused kernel's average duration
+    between those events (which include its dispatch) and its roofline fraction (its algorithmic
+    bytes: everything the call moves except the gradWeight write, which the reduction kernel does,
+    unless the fused kernel writes gradWeight itself). `flat_stream` is torch's elementwise
+    gradY + x into a third tensor of the same shape (the backward's 2 reads and 1 write with no
+    stencil, mask or reduction), timed the same way, and the backward against it. `traffic` is the
+    fused kernel's HBM bytes per launch from the committed counter summary for this workload
+    (null when there is none for the built kernel source)."""
     import statistics
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -192,6 +207,9 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
                 times.append(e0.elapsed_time(e1))
         return statistics.median(times), min(times)
 
+    def pct(nbytes, ms):
+        return round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+
     rows = []
     for wlc in workloads:
         gy_c = wls.full_tensor(wlc, wls.STREAM_GY, dev)
@@ -200,22 +218,44 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
         gx_c, gw_c, y_c = torch.empty_like(gy_c), torch.empty_like(w_c), torch.empty_like(x_c)
         ws_c = mdc.workspace_for(wlc.S, wlc.B, wlc.H, gy_c.dtype, dev)
         torch.cuda.synchronize()
-        b_med, b_min = per_call(lambda: mdc.backward(gy_c, x_c, w_c, m_c, gradX=gx_c,
-                                                     gradWeight=gw_c, workspace=ws_c,
-                                                     stream=stream))
+        bwd = lambda: mdc.backward(gy_c, x_c, w_c, m_c, gradX=gx_c, gradWeight=gw_c,  # noqa: E731
+                                   workspace=ws_c, stream=stream)
+        b_med, b_min = per_call(bwd)
+        # a second pass of the same per-call timing with the library's kernel events on (they add
+        # their own time to the call, so the call's own figure comes from the pass above)
+        mdc.mccb_profile_begin(reps + 2)
+        per_call(bwd)
+        k1_ms, k2_ms, n_prof = mdc.mccb_profile_end()
         f_med, f_min = per_call(lambda: mdc.forward(x_c, w_c, m_c, y=y_c, stream=stream))
+        s_med, _ = per_call(lambda: torch.add(gy_c, x_c, out=gx_c))
         b_alg = wlc.algorithmic_bytes()
+        # with one strip of one batch (no workspace) the fused kernel writes gradWeight itself
+        direct = mdc.mccb_get_workspace_size(wlc.S, wlc.B, wlc.H, mdc.DTYPE_CODE[gy_c.dtype]) == 0
+        k1_alg = b_alg - (0 if direct else 3 * wlc.H * 2)
         f_alg = 4 * wlc.N + (wlc.B * wlc.S if m_c is not None else 0) + 3 * wlc.H * 2
+        s_alg = 3 * wlc.N * 2
+        k1_avg = k1_ms / max(n_prof, 1)
         rows.append({
             "workload": wlc.describe(),
             "backward": {"median_ms": round(b_med, 5), "min_ms": round(b_min, 5),
                          "gbs": round(b_alg / (b_med * 1e-3) / 1e9, 1),
-                         "pct_of_hbm_peak": round(100 * b_alg / (b_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+                         "pct_of_hbm_peak": pct(b_alg, b_med),
+                         "fused_kernel": {"avg_ms": round(k1_avg, 5),
+                                          "algorithmic_bytes": k1_alg,
+                                          "frac": round(pct(k1_alg, k1_avg) / 100, 4),
+                                          "traffic": measured_traffic(
+                                              wlc.name, traffic_file("mccb_fused_bwd", wlc.name))},
+                         "reduce_kernel_avg_ms": round(k2_ms / max(n_prof, 1), 5),
+                         "flat_stream": {"median_ms": round(s_med, 5),
+                                         "pct_of_hbm_peak": pct(s_alg, s_med),
+                                         "backward_pct_of_flat_stream": round(
+                                             100 * pct(b_alg, b_med) / pct(s_alg, s_med), 2)}},
             "forward": {"median_ms": round(f_med, 5), "min_ms": round(f_min, 5),
                         "gbs": round(f_alg / (f_med * 1e-3) / 1e9, 1),
-                        "pct_of_hbm_peak": round(100 * f_alg / (f_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
+                        "pct_of_hbm_peak": pct(f_alg, f_med)},
         })
-        log(f"config {wlc.name}: backward {b_med:.4f} ms, forward {f_med:.4f} ms")
+        log(f"config {wlc.name}: backward {b_med:.4f} ms (fused kernel {k1_avg:.4f}), forward "
+            f"{f_med:.4f} ms, flat stream {s_med:.4f} ms")
         del gy_c, x_c, w_c, m_c, gx_c, gw_c, y_c, ws_c
         torch.cuda.empty_cache()
     del flush
@@ -308,6 +348,9 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(wl.name), "algorithmic_bytes": fused_alg,
                 "kernel": "mccb_fused_bwd", "avg_ms": round(fused_avg_ms, 5),
+                "timing_source": ("HIP events the library records on the launch stream around "
+                                  "the fused kernel (mccb_profile_begin/_end), averaged over the "
+                                  f"{n_prof} timed steps"),
                 "reduce_avg_ms": round(reduce_ms / max(n_prof, 1), 5)}
 
     fwd = None

@@ -165,11 +165,14 @@ typedef struct {
  * now"; the kernels here take W = 1..4 (other values: MCCB_ERR_SHAPE). W = 3 with NULL strides is
  * exactly mccb_get_workspace_size / mccb_backward / mccb_forward.
  *
- * Strides (NULL = all contiguous): an input whose channels are contiguous (H stride 1) with even
- * row and batch strides and a 4-byte aligned base is read in place by the backward; any other
- * gradY or x is first packed into a contiguous copy inside the workspace (one extra read and write
- * of that tensor), and a weight that is not contiguous and 16-byte aligned is packed too. The mask
- * is read through its strides. Phase 1 therefore takes the input pointers as well (as the page's
+ * Strides (NULL = all contiguous): the backward reads gradY or x in place when its channels are
+ * contiguous (H stride 1), its row and batch strides are multiples of the fused kernel's lane
+ * width in elements, its base is aligned to the lane width in bytes, and a wave's columns span
+ * less than 4 GiB of it. The lane width is 8 bytes (4 elements) on shapes with S > 64, W <= 3 and
+ * B*H a multiple of 32768, and 4 bytes (2 elements) on all others. Any other gradY or x is first
+ * packed into a contiguous copy inside the workspace (one extra read and write of that tensor),
+ * and a weight that is not contiguous and 16-byte aligned is packed too; phase 1 includes those
+ * copies in the size it reports. The mask is read through its strides. Phase 1 therefore takes the input pointers as well (as the page's
  * phase 1 takes the tensors): they are inspected for alignment only, never dereferenced. Input
  * bases need 2-byte alignment; gradX, gradWeight and the workspace stay contiguous and 16-byte
  * aligned. Negative strides, or an input extent past 2^62 bytes, give MCCB_ERR_PARAM_INVALID; no

@@ -164,26 +164,36 @@ struct Vec {
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
 //        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
 //        4-tap windows).
-constexpr int kLayoutRing = 0, kLayoutWide = 1, kLayoutNarrowRing = 2;
+constexpr int kLayoutRing = 0, kLayoutWide = 1, kLayoutNarrowRing = 2, kLayoutTall = 3;
+// The tall layout (sequences of at most kTallRows rows, one strip): 8 ring waves on one column group
+// take every row of the strip in a single round, so a block's loads all go out together.
+constexpr int kTallWaves = 8;
+constexpr int kTallRows = kTallWaves * kTurnRows;
 template <int W, bool STRIDED, int LAYOUT>
 struct FusedCfg {
     static constexpr bool WIDE = LAYOUT == kLayoutWide;
+    static constexpr bool TALL = LAYOUT == kLayoutTall;
     static constexpr bool tight = (STRIDED && W >= 3) || W > 3;
     static constexpr int V = WIDE ? MCCB_WIDE_VEC : 2;  // columns per lane
     static constexpr int CG = WIDE ? MCCB_WIDE_COL_GROUPS
-                                   : ((tight || LAYOUT == kLayoutNarrowRing) ? 2 : MCCB_RING_COL_GROUPS);
-    static constexpr int RG = WIDE ? MCCB_WIDE_RING : 2;  // waves per column group
+                              : TALL ? 1
+                                     : ((tight || LAYOUT == kLayoutNarrowRing) ? 2 : MCCB_RING_COL_GROUPS);
+    static constexpr int RG = WIDE ? MCCB_WIDE_RING : TALL ? kTallWaves : 2;  // waves per column group
     static constexpr int WPS = WIDE ? MCCB_WIDE_WAVES_PER_SIMD : (tight ? 3 : 4);
     static constexpr int GC = kWave * V;       // columns of one column group
     static constexpr int BW = CG * RG;         // waves per block
     static constexpr int RR = RG * kTurnRows;  // rows a block advances per round
+    // longest strip a block of this layout walks (the mask staging is unrolled for it)
+    static constexpr int MAX_STRIP = TALL ? kTallRows : kPlanMaxStripRows;
     // column groups spaced this many lane vectors apart (0: adjacent)
     static constexpr int64_t DLV = WIDE ? (int64_t)MCCB_GROUP_SPACING / (V * 2) : 0;
     static_assert(!WIDE || W <= 3, "the wide layout holds at most 3 taps of fp64 state");
     static_assert(V == 2 || V == 4, "lane vector must be 4 or 8 bytes");
     static_assert(GC < 384, "a column group spans at most 2 batches (H >= 384)");
     static_assert(CG <= 8, "the staged mask holds two batches for each of at most 8 groups");
-    static_assert(kPlanRound % RR == 0, "strips must be whole rounds");
+    // a turn never straddles the end of a strip other than the tensor's last row: strips are whole
+    // rounds (the tall layout has a single strip)
+    static_assert(TALL || kPlanRound % RR == 0, "strips must be whole rounds");
     static_assert(BW * kWave <= 1024, "block too large");
     static_assert(DLV % kWave == 0, "group spacing must be a whole number of wave-wide loads");
 };
@@ -329,6 +339,16 @@ __device__ static inline typename Vec<V>::t stencil_row(const double (&d)[W][V],
     return r;
 }
 
+// gradWeight entries, rounded once: round-to-odd to fp32, then nearest-even to the dtype.
+template <int DT>
+__device__ static inline void store_gw(uint16_t *p, double t) {
+    *p = (uint16_t)(Fmt<DT>::pack(round_to_odd_f32(t), 0.0f) & 0xFFFFu);
+}
+template <int DT>
+__device__ static inline void store_gw(uint16_t *p, f64x2 t) {  // p 4-byte aligned
+    *reinterpret_cast<uint32_t *>(p) = Fmt<DT>::pack(round_to_odd_f32(t[0]), round_to_odd_f32(t[1]));
+}
+
 template <int DT, int V>
 __device__ static inline void widen(const typename Vec<V>::t q, double (&d)[V]) {
     float f[V];
@@ -382,8 +402,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
                    const void *__restrict__ w_, const uint8_t *__restrict__ mask,
                    void *__restrict__ gx_, double *__restrict__ ws, int64_t S, int64_t B, int64_t H,
                    int64_t rows_per_strip, int64_t n_col_blocks, int64_t n_sp_blocks,
-                   InStrides st, const uint8_t *__restrict__ ahead = nullptr, int lim_lds = 0) {
+                   InStrides st, const uint8_t *__restrict__ ahead, int lim_lds,
+                   uint16_t *__restrict__ gw_direct) {
     typedef FusedCfg<W, STRIDED, LAYOUT> Cfg;
+    static_assert(!(Cfg::TALL && VARLEN), "the packed layout does not take the tall blocks");
     constexpr int V = Cfg::V, CG = Cfg::CG, RG = Cfg::RG, TR = kTurnRows, RR = Cfg::RR;
     typedef typename Vec<V>::t vec_t;
     constexpr int L = W - 1;  // look-ahead rows
@@ -414,6 +436,51 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 
     const int span = (int)(rows_per_strip + L);  // rows of the strip and its look-ahead
     const int mspan = (int)(rows_per_strip + kMaskPad);  // bytes of one staged mask slot
+    // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
+    // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
+    const int64_t row_bytes = C * 2;
+    const uint32_t lane_off = (uint32_t)(v * (V * 2));
+    // STRIDED: the wave's first batch goes into the uniform base, the lane keeps the rest
+    const char *gy_base = reinterpret_cast<const char *>(gy_) + (STRIDED ? jg * st.gy_batch * 2 : 0);
+    const char *x_base = reinterpret_cast<const char *>(x_) + (STRIDED ? jg * st.x_batch * 2 : 0);
+    const int64_t gy_rb = STRIDED ? st.gy_row * 2 : row_bytes;
+    const int64_t x_rb = STRIDED ? st.x_row * 2 : row_bytes;
+    const uint32_t gy_lane = STRIDED ? (uint32_t)(((j - jg) * st.gy_batch + h) * 2) : lane_off;
+    const uint32_t x_lane = STRIDED ? (uint32_t)(((j - jg) * st.x_batch + h) * 2) : lane_off;
+    auto at_gy = [&](int64_t row) -> const vec_t * {
+        return reinterpret_cast<const vec_t *>(gy_base + row * gy_rb + gy_lane);
+    };
+    auto at_x = [&](int64_t row) -> const vec_t * {
+        return reinterpret_cast<const vec_t *>(x_base + row * x_rb + x_lane);
+    };
+    auto out_at = [&](int64_t row) -> vec_t * {
+        return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx_) + row * row_bytes + lane_off);
+    };
+    // The loads of one turn (gradY rows i0 .. i0+TR+L-1, x rows i0 .. i0+TR-1); CLAMP: a row past
+    // the tensor's last row S-1 is read at row S-1, a valid address, and cleared before use.
+    auto issue_rows = [&](auto clamp_tag, int64_t i0, vec_t(&qy)[TR + L], vec_t(&qx)[TR]) {
+        constexpr bool CLAMP = decltype(clamp_tag)::value;
+        auto row = [&](int64_t r) -> int64_t {
+            if constexpr (CLAMP) return r < S - 1 ? r : S - 1;
+            return r;
+        };
+#pragma unroll
+        for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(at_gy(row(i0 + k)));
+#pragma unroll
+        for (int u = 0; u < TR - L; ++u) qy[u + L] = load_gy_stream(at_gy(row(i0 + L + u)));
+#pragma unroll
+        for (int u = TR - L; u < TR; ++u) qy[u + L] = load_vec_cached(at_gy(row(i0 + L + u)));
+#pragma unroll
+        for (int u = 0; u < TR; ++u) qx[u] = load_vec(at_x(row(i0 + u)));
+    };
+    // The tall layout's blocks live a single round: each wave's one turn (clamped near the end of
+    // the tensor) goes out before the mask staging, so that one round trip covers both.
+    vec_t ty[TR + L], tx[TR];
+    const int64_t t_i0 = rs0 + ring * TR;
+    if constexpr (Cfg::TALL) {
+        if (t_i0 < rs1) issue_rows(std::true_type{}, t_i0, ty, tx);
+    }
+
     int moff = 0;  // offset of this lane's batch in the staged mask
     if constexpr (HAS_MASK) {
         // Each column group stages the bytes of its (at most two) batches: [CG][2][mspan], 0xFF
@@ -436,7 +503,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         // Slot (gg, b) holds bytes rs0 .. rs0+mspan-1 of mask row jf[gg] + b; a thread takes bytes
         // tid, tid + kThreads, ... of every slot. The slot's batch is the same for the whole block.
         constexpr int kThreads = Cfg::BW * kWave;
-        constexpr int kPer = (kPlanMaxStripRows + kMaskPad + kThreads - 1) / kThreads;
+        constexpr int kPer = (Cfg::MAX_STRIP + kMaskPad + kThreads - 1) / kThreads;
         uint8_t vals[2 * CG][kPer];
 #pragma unroll
         for (int slot = 0; slot < 2 * CG; ++slot) {
@@ -523,27 +590,6 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         return r;
     };
 
-    // Wave-uniform row addresses plus one 32-bit lane offset: loads and stores take the
-    // scalar-base + vector-offset form, with no per-lane 64-bit address arithmetic.
-    const int64_t row_bytes = C * 2;
-    const uint32_t lane_off = (uint32_t)(v * (V * 2));
-    // STRIDED: the wave's first batch goes into the uniform base, the lane keeps the rest
-    const char *gy_base = reinterpret_cast<const char *>(gy_) + (STRIDED ? jg * st.gy_batch * 2 : 0);
-    const char *x_base = reinterpret_cast<const char *>(x_) + (STRIDED ? jg * st.x_batch * 2 : 0);
-    const int64_t gy_rb = STRIDED ? st.gy_row * 2 : row_bytes;
-    const int64_t x_rb = STRIDED ? st.x_row * 2 : row_bytes;
-    const uint32_t gy_lane = STRIDED ? (uint32_t)(((j - jg) * st.gy_batch + h) * 2) : lane_off;
-    const uint32_t x_lane = STRIDED ? (uint32_t)(((j - jg) * st.x_batch + h) * 2) : lane_off;
-    auto at_gy = [&](int64_t row) -> const vec_t * {
-        return reinterpret_cast<const vec_t *>(gy_base + row * gy_rb + gy_lane);
-    };
-    auto at_x = [&](int64_t row) -> const vec_t * {
-        return reinterpret_cast<const vec_t *>(x_base + row * x_rb + x_lane);
-    };
-    auto out_at = [&](int64_t row) -> vec_t * {
-        return reinterpret_cast<vec_t *>(reinterpret_cast<char *>(gx_) + row * row_bytes + lane_off);
-    };
-
     // A turn is "whole" when this wave's TR rows and their look-ahead rows all exist.
     auto whole = [&](int64_t r0) {
         const int64_t i0 = r0 + ring * TR;
@@ -556,15 +602,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     // (Each kind of load has a loop of its own: a choice between a cached and a streaming load
     // of one address inside one loop body is merged into a single plain load by the compiler.)
     auto issue = [&](int64_t r0, vec_t (&qy)[TR + L], vec_t (&qx)[TR]) {
-        const int64_t i0 = r0 + ring * TR;
-#pragma unroll
-        for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(at_gy(i0 + k));
-#pragma unroll
-        for (int u = 0; u < TR - L; ++u) qy[u + L] = load_gy_stream(at_gy(i0 + L + u));
-#pragma unroll
-        for (int u = TR - L; u < TR; ++u) qy[u + L] = load_vec_cached(at_gy(i0 + L + u));
-#pragma unroll
-        for (int u = 0; u < TR; ++u) qx[u] = load_vec(at_x(i0 + u));
+        issue_rows(std::false_type{}, r0 + ring * TR, qy, qx);
     };
     auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
         const int64_t i0 = r0 + ring * TR;
@@ -631,16 +669,58 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         __builtin_amdgcn_s_barrier();
     };
 
-    vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
-    if (whole(rs0)) issue(rs0, ay, ax);
-    // Unrolled by two so that the two register buffers swap roles without copies.
-    for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
-        round(r0, ay, ax, by, bx);
-        if (r0 + RR >= rs1) break;
-        round(r0 + RR, by, bx, ay, ax);
+    if constexpr (Cfg::TALL) {
+        // One round covers the strip. A turn that reaches past row S-1 clears the rows past it
+        // (the staged mask already holds 0 there) and stores only rows inside the strip; its x
+        // rows past S-1 meet only cleared gradY rows and add nothing to gradWeight.
+        if (t_i0 < rs1) {
+            uint32_t mw[4];
+            turn_mask(t_i0, mw);
+            if constexpr (!HAS_MASK) {
+                const int64_t nv = S - t_i0;  // rows of the turn that exist, >= 1
+                const uint64_t lo = nv >= 8 ? ~0ull : (1ull << (8 * nv)) - 1u;
+                const uint64_t hi = nv >= 16 ? ~0ull : nv <= 8 ? 0ull : (1ull << (8 * (nv - 8))) - 1u;
+                mw[0] = (uint32_t)lo;
+                mw[1] = (uint32_t)(lo >> 32);
+                mw[2] = (uint32_t)hi;
+                mw[3] = (uint32_t)(hi >> 32);
+            }
+            auto clear = [&](const vec_t &q, int k) -> vec_t {
+                const uint32_t m = (uint32_t)((int32_t)(mw[k >> 2] << (24 - 8 * (k & 3))) >> 24);
+                vec_t r;
+#pragma unroll
+                for (int p = 0; p < V / 2; ++p) r[p] = q[p] & m;
+                return r;
+            };
+            double d[W][V];
+#pragma unroll
+            for (int k = 0; k < L; ++k) widen<DT, V>(clear(ty[k], k), d[k]);
+#pragma unroll
+            for (int u = 0; u < TR; ++u) {
+                widen<DT, V>(clear(ty[u + L], u + L), d[L]);
+                const vec_t r = stencil_row<DT, W, V>(d, tx[u], wt, a);
+                if (active && t_i0 + u < rs1) store_vec(out_at(t_i0 + u), r);
+#pragma unroll
+                for (int k = 0; k < L; ++k)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
+            }
+        }
+    } else {
+        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        if (whole(rs0)) issue(rs0, ay, ax);
+        // Unrolled by two so that the two register buffers swap roles without copies.
+        for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
+            round(r0, ay, ax, by, bx);
+            if (r0 + RR >= rs1) break;
+            round(r0 + RR, by, bx, ay, ax);
+        }
     }
 
-    // gradWeight partials of the strip, one fp64 value per (tap, column).
+    // gradWeight partials of the strip, one fp64 value per (tap, column); or, with gw_direct (one
+    // strip and one batch: the block's sums are the whole gradWeight of its channels), gradWeight
+    // itself, rounded once. The reduction kernel would add the partial to a zero sum: adding +0.0
+    // here gives the same bits.
     if constexpr (RG == 1) {
         // one wave per column group: the lane's own sums are the partials
         if (active) {
@@ -667,7 +747,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
                     f64x2 sum = red[group][lane * (V / 2) + p];
 #pragma unroll
                     for (int q = 1; q < RG; ++q) sum += red[q * CG + group][lane * (V / 2) + p];
-                    *reinterpret_cast<f64x2 *>(ws + (strip * W + k) * C + c + 2 * p) = sum;
+                    if (gw_direct)
+                        store_gw<DT>(gw_direct + k * H + c + 2 * p, sum + f64x2{0.0, 0.0});
+                    else
+                        *reinterpret_cast<f64x2 *>(ws + (strip * W + k) * C + c + 2 * p) = sum;
                 }
             }
         }
@@ -682,15 +765,6 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 // in wave order. The order of every channel's sum depends only on (n_strips, B), not on
 // kReduceVec.
 // ---------------------------------------------------------------------------------------------
-template <int DT>
-__device__ static inline void store_gw(uint16_t *p, double t) {
-    *p = (uint16_t)(Fmt<DT>::pack(round_to_odd_f32(t), 0.0f) & 0xFFFFu);
-}
-template <int DT>
-__device__ static inline void store_gw(uint16_t *p, f64x2 t) {  // p 4-byte aligned
-    *reinterpret_cast<uint32_t *>(p) = Fmt<DT>::pack(round_to_odd_f32(t[0]), round_to_odd_f32(t[1]));
-}
-
 template <int DT>
 __global__ void __launch_bounds__(kReduceWaves *kWave)
     mccb_gw_reduce(const double *__restrict__ ws, uint16_t *__restrict__ gw, int64_t n_strips,
@@ -1040,6 +1114,9 @@ struct Plan {
     int64_t S, B, H, C;
     int dtype, W;
     int64_t rows_per_strip, n_strips, n_col_blocks;
+    // one strip and one batch: the fused kernel's block sums are whole gradWeight entries, so it
+    // writes gradWeight itself and the reduction kernel (and the workspace) is not needed
+    bool direct;
     uint64_t ws_bytes;
     size_t mask_lds;
 };
@@ -1087,7 +1164,8 @@ Plan make_plan(int64_t S, int64_t B, int64_t H, int dtype, int W = 3) {
         ++strips;  // keep the staged mask within its LDS budget
     }
     p.n_strips = (S + p.rows_per_strip - 1) / p.rows_per_strip;
-    p.ws_bytes = (uint64_t)p.n_strips * (uint64_t)W * (uint64_t)p.C * sizeof(double);
+    p.direct = p.n_strips == 1 && B == 1;
+    p.ws_bytes = p.direct ? 0u : (uint64_t)p.n_strips * (uint64_t)W * (uint64_t)p.C * sizeof(double);
     return p;
 }
 
@@ -1133,16 +1211,19 @@ bool fused_wide(int64_t C, int64_t W) {
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).
-int fused_vec(int64_t C, int64_t W) {
-    return fused_wide(C, W) ? FusedCfg<3, false, kLayoutWide>::V : FusedCfg<3, false, kLayoutRing>::V;
+int fused_vec(int64_t S, int64_t C, int64_t W) {
+    return (S > kTallRows && fused_wide(C, W)) ? FusedCfg<3, false, kLayoutWide>::V
+                                               : FusedCfg<3, false, kLayoutRing>::V;
 }
 
-// The layout a fused launch takes: wide (above), else the ring; the narrow ring (2 column groups
+// The layout a fused launch takes: tall for sequences of at most kTallRows rows (one strip, which
+// its 8 ring waves cover in one round), else wide (above), else the ring; the narrow ring (2 column groups
 // instead of 4, so twice the blocks) when the ring's grid would stay under the plan's block target
 // (the 128-row floor on strips stopped the plan short of it), and the ring is not already narrow
 // (strided 3-tap, 4-tap). The column groups of a block do not enter any column's summation
 // order, so the narrow ring's results equal the ring's bit for bit.
 int fused_layout(const Plan &p, bool strided, bool varlen) {
+    if (!varlen && p.S <= kTallRows) return kLayoutTall;  // one strip, one round
     if (!varlen && fused_wide(p.C, p.W)) return kLayoutWide;
     const bool tight = (strided && p.W >= 3) || p.W > 3;
     if (!tight && fused_grid<3, false, kLayoutRing>(p.C).ncb * p.n_strips < kMinBlocks)
@@ -1153,13 +1234,18 @@ int fused_layout(const Plan &p, bool strided, bool varlen) {
 template <int DT, bool M, bool T, int TAPS, bool VL, int LAYOUT>
 hipError_t launch_fused(const Plan &p, const void *gy, const void *x, const void *w,
                         const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
-                        const InStrides &is, const uint8_t *ahead, int lim_lds) {
+                        const InStrides &is, const uint8_t *ahead, int lim_lds, void *gw_direct) {
+    typedef FusedCfg<TAPS, T, LAYOUT> Cfg;
+    // the kernel's assumptions: turns never straddle an inner strip end, the tall layout has one
+    // strip, and a direct gradWeight write needs the in-block sum over several ring waves
+    if ((!Cfg::TALL && p.rows_per_strip % Cfg::RR != 0) || (Cfg::TALL && p.n_strips != 1) ||
+        (gw_direct && Cfg::RG < 2))
+        return hipErrorInvalidValue;
     const FusedGrid fg = fused_grid<TAPS, T, LAYOUT>(p.C);
     hipLaunchKernelGGL((mccb_fused_bwd<DT, M, T, TAPS, VL, LAYOUT>),
-                       dim3((unsigned)(fg.ncb * p.n_strips)),
-                       dim3(FusedCfg<TAPS, T, LAYOUT>::BW * kWave), lds, st, gy, x, w, mask, gx,
-                       (double *)ws, p.S, p.B, p.H, p.rows_per_strip, fg.ncb, fg.n_sp, is, ahead,
-                       lim_lds);
+                       dim3((unsigned)(fg.ncb * p.n_strips)), dim3(Cfg::BW * kWave), lds, st, gy,
+                       x, w, mask, gx, (double *)ws, p.S, p.B, p.H, p.rows_per_strip, fg.ncb,
+                       fg.n_sp, is, ahead, lim_lds, (uint16_t *)gw_direct);
     return hipGetLastError();
 }
 
@@ -1167,31 +1253,36 @@ template <int DT, bool M, bool T, int TAPS, bool VL>
 hipError_t launch_fused_layout(int layout, const Plan &p, const void *gy, const void *x,
                                const void *w, const uint8_t *mask, void *gx, void *ws,
                                hipStream_t st, size_t lds, const InStrides &is,
-                               const uint8_t *ahead, int lim_lds) {
+                               const uint8_t *ahead, int lim_lds, void *gw_direct) {
+    if constexpr (!VL) {
+        if (layout == kLayoutTall)
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutTall>(p, gy, x, w, mask, gx, ws, st,
+                                                                 lds, is, ahead, lim_lds, gw_direct);
+    }
     if constexpr (TAPS <= 3 && !VL) {
         if (layout == kLayoutWide)
             return launch_fused<DT, M, T, TAPS, VL, kLayoutWide>(p, gy, x, w, mask, gx, ws, st,
-                                                                 lds, is, ahead, lim_lds);
+                                                                 lds, is, ahead, lim_lds, gw_direct);
     }
     if constexpr (!((T && TAPS >= 3) || TAPS > 3)) {  // instantiated where the ring is not narrow
         if (layout == kLayoutNarrowRing)
-            return launch_fused<DT, M, T, TAPS, VL, kLayoutNarrowRing>(p, gy, x, w, mask, gx, ws,
-                                                                       st, lds, is, ahead, lim_lds);
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutNarrowRing>(
+                p, gy, x, w, mask, gx, ws, st, lds, is, ahead, lim_lds, gw_direct);
     }
     return launch_fused<DT, M, T, TAPS, VL, kLayoutRing>(p, gy, x, w, mask, gx, ws, st, lds, is,
-                                                         ahead, lim_lds);
+                                                         ahead, lim_lds, gw_direct);
 }
 
 // One fused launch for any (mask, strided, W) of the padded layouts (VL false) or the packed one.
 template <int DT, bool VL>
 hipError_t launch_fused_any(const Plan &p, const void *gy, const void *x, const void *w,
                             const uint8_t *mask, void *gx, void *ws, hipStream_t st, size_t lds,
-                            const InStrides &is, bool strided, const uint8_t *ahead = nullptr,
-                            int lim_lds = 0) {
+                            const InStrides &is, bool strided, const uint8_t *ahead,
+                            int lim_lds, void *gw_direct) {
     const int layout = fused_layout(p, strided, VL);
 #define MCCB_FUSED(M, T, TAPS)                                                                    \
     return launch_fused_layout<DT, M, T, TAPS, VL>(layout, p, gy, x, w, mask, gx, ws, st, lds, is, \
-                                                   ahead, lim_lds)
+                                                   ahead, lim_lds, gw_direct)
 #define MCCB_FUSED_W(TAPS)                                                                        \
     if constexpr (!VL) {                                                                          \
         if (strided) {                                                                            \
@@ -1219,9 +1310,14 @@ hipError_t launch(const Plan &p, const void *gy, const void *x, const void *w, c
     const size_t lds_floor = MCCB_LDS_FLOOR;
     const size_t lds = mask ? (p.mask_lds > lds_floor ? p.mask_lds : lds_floor) : lds_floor;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hipErrorInvalidValue;
-    hipError_t e = launch_fused_any<DT, false>(p, gy, x, w, mask, gx, ws, st, lds, is, strided);
+    hipError_t e = launch_fused_any<DT, false>(p, gy, x, w, mask, gx, ws, st, lds, is, strided,
+                                               nullptr, 0, p.direct ? gw : nullptr);
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hipErrorInvalidValue;
+    if (p.direct) {  // gradWeight already written
+        if (ev && hipEventRecord(ev[2], st) != hipSuccess) return hipErrorInvalidValue;
+        return hipSuccess;
+    }
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
@@ -1425,8 +1521,9 @@ hipError_t launch_varlen_bwd(const Plan &p, const void *gy, const void *x, const
     const int lim_lds = mask ? (int)p.mask_lds : 0;
     const size_t lds = (size_t)lim_lds + (size_t)span;
     const InStrides is{p.H, p.H, p.H, p.H, T, 1};
-    e = launch_fused_any<DT, true>(p, gy, x, w, mask, gx, ws, st, lds, is, false, ahead, lim_lds);
-    if (e != hipSuccess) return e;
+    e = launch_fused_any<DT, true>(p, gy, x, w, mask, gx, ws, st, lds, is, false, ahead, lim_lds,
+                                   p.direct ? gw : nullptr);
+    if (e != hipSuccess || p.direct) return e;
     const dim3 grid2((unsigned)((p.H + kReduceCols - 1) / kReduceCols), (unsigned)p.W);
     const dim3 block2(kReduceWaves * kWave);
     hipLaunchKernelGGL((mccb_gw_reduce<DT>), grid2, block2, 0, st, (const double *)ws,
@@ -1592,10 +1689,16 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     typedef FusedCfg<3, false, kLayoutWide> Wd;
     typedef FusedCfg<3, false, kLayoutRing> Rg;
     typedef FusedCfg<3, false, kLayoutNarrowRing> Nr;
+    typedef FusedCfg<3, false, kLayoutTall> Tl;
     plan->rows_per_turn = kTurnRows;
     plan->rows_per_strip = p.rows_per_strip;
     plan->n_strips = p.n_strips;
-    if (layout == kLayoutWide) {
+    if (layout == kLayoutTall) {
+        plan->rows_per_round = Tl::RR;
+        plan->cols_per_block = Tl::CG * Tl::GC;
+        plan->n_col_blocks = fused_grid<3, false, kLayoutTall>(p.C).ncb;
+        plan->waves_per_block = Tl::BW;
+    } else if (layout == kLayoutWide) {
         plan->rows_per_round = Wd::RR;
         plan->cols_per_block = Wd::CG * Wd::GC;
         plan->n_col_blocks = fused_grid<3, false, kLayoutWide>(p.C).ncb;
@@ -1685,7 +1788,7 @@ int mccb_get_workspace_size_ex(const void *gradY, const void *x, const void *wei
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype, (int)W);
     *workspace_size =
-        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(B * H, W), kLaneSpan).total;
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(S, B * H, W), kLaneSpan).total;
     return MCCB_OK;
 }
 
@@ -1702,7 +1805,7 @@ int mccb_backward_ex(const void *gradY, const void *x, const void *weight, const
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype, (int)W);
     const ExLayout L =
-        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(B * H, W), kLaneSpan);
+        ex_layout(p.ws_bytes, S, B, H, W, &a.gy, a.x, weight, a.w0, a.w1, fused_vec(S, B * H, W), kLaneSpan);
     if (L.total > 0 && !workspace) return MCCB_ERR_PARAM_NULLPTR;
     if (workspace_size < L.total) return MCCB_ERR_PARAM_INVALID;
     if (!aligned16(gradX) || !aligned16(gradWeight) || (L.total > 0 && !aligned16(workspace)))

@@ -100,8 +100,10 @@ def test_shape_out_of_range(S, B, H):
 @pytest.mark.parametrize("S,B,H", [(1, 1, 384), (524288, 1, 384), (16384, 32, 5120),
                                    (262144, 2, 24576), (1, 32, 24576), (3, 7, 448)])
 def test_shape_limits_accepted(S, B, H):
-    # the limits themselves are valid (constraints section: B 1..32, B*S 1..512K, H 384..24576)
-    assert _ws(S, B, H) > 0
+    # the limits themselves are valid (constraints section: B 1..32, B*S 1..512K, H 384..24576);
+    # one strip of one batch needs no workspace (the fused kernel writes gradWeight itself)
+    p = mdc.mccb_get_plan(S, B, H, BF16)
+    assert (_ws(S, B, H) == 0) == (B == 1 and p["n_strips"] == 1)
 
 
 def test_workspace_too_small():
@@ -216,11 +218,16 @@ def test_plan_is_pure_and_consistent():
         p2 = mdc.mccb_get_plan(S, B, H, dt)
         assert p1 == p2
         C = B * H
-        assert p1["rows_per_strip"] % p1["rows_per_round"] == 0
+        if S <= 64:  # the tall layout: one strip, which one round of 8 ring waves covers
+            assert p1["n_strips"] == 1 and p1["waves_per_block"] == 8
+            assert p1["rows_per_round"] == 64 >= p1["rows_per_strip"]
+        else:
+            assert p1["rows_per_strip"] % p1["rows_per_round"] == 0
         assert p1["rows_per_round"] % p1["rows_per_turn"] == 0
         assert p1["n_strips"] == -(-S // p1["rows_per_strip"])
         assert p1["n_col_blocks"] == -(-C // p1["cols_per_block"])
-        assert p1["workspace_size"] == p1["n_strips"] * 3 * C * 8
+        direct = B == 1 and p1["n_strips"] == 1  # gradWeight written by the fused kernel
+        assert p1["workspace_size"] == (0 if direct else p1["n_strips"] * 3 * C * 8)
         assert p1["workspace_size"] == _ws(S, B, H, dt)
         # the plan does not depend on the dtype
         other = FP16 if dt == BF16 else BF16
@@ -314,6 +321,25 @@ def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
     assert mdc.mccb_forward_get_workspace_size_ex(X + 8, W, S, B, H, 3, BF16, None) == nb
     assert mdc.mccb_forward_get_workspace_size_ex(X, W, S, B, H, 3, BF16,
                                                   strides(x=[B * H + 2, H, 1])) == nb
+
+
+def test_ex_lane_width_decides_in_place_reads():
+    """The in-place rule follows the fused kernel's lane width: 8 bytes on shapes with S > 64,
+    W <= 3 and B*H a multiple of 32768, 4 bytes elsewhere. Even strides and a 4-byte (not 8-byte)
+    aligned base are read in place on a 4-byte-lane shape and packed on an 8-byte-lane shape."""
+    for S, B, H, wide in [(128, 8, 4096, True), (64, 8, 4096, False), (128, 3, 4096, False)]:
+        base, nb = _ws(S, B, H), S * B * H * 2
+        packed = -(-base // 256) * 256 + nb
+        gy4 = GY + 4  # 4-byte aligned, not 8
+        got = mdc.mccb_get_workspace_size_ex(gy4, X, W, S, B, H, 3, BF16, None)
+        assert got == (packed if wide else base), (S, B, H)
+        # row and batch strides of 2 elements more than contiguous: multiples of 2, not of 4
+        st = strides(S, B, H, gy=[B * (H + 2), H + 2, 1])
+        got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 3, BF16, st)
+        assert got == (packed if wide else base), (S, B, H)
+        # W = 4 never takes the 8-byte lanes
+        got = mdc.mccb_get_workspace_size_ex(gy4, X, W, S, B, H, 4, BF16, None)
+        assert got == mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 4, BF16, None)
 
 
 @pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
@@ -437,7 +463,8 @@ def test_varlen_validation():
     assert vcall(dt=2) == INVALID
     assert vcall(cu=CU + 4) == INVALID  # int64 array must be 8-byte aligned
     assert vcall(x=X + 8) == INVALID
-    assert vcall(wsz=100) == INVALID
+    need = mdc.mccb_varlen_get_workspace_size(100, 3, 384, 3, BF16)
+    assert vcall(wsz=need - 1) == INVALID
     assert vcall(gx=CU - 64) == INVALID  # gradX overlapping cu_seqlens
     assert vcall(ws=X + 4096) == INVALID
     rc = mdc.mccb_varlen_forward(X, W, M, CU, X + 4096, 100, 3, 384, 3, BF16, WS, 1 << 40, None)

@@ -137,3 +137,28 @@ def test_max_sequence_length_sampled():
     from .test_forward import gpu_forward
     y = gpu_forward(wl, (inputs[1], inputs[2], inputs[3]))
     fwd_columns(wl, y, hs)
+
+
+@pytest.mark.parametrize("S,dtype,mask", [(64, "bf16", ("bernoulli", 0.8)), (37, "fp16", ("null",)),
+                                          (128, "bf16", ("prefix",)), (1, "bf16", ("null",))])
+def test_direct_gradweight_equals_two_kernel_path(S, dtype, mask):
+    """One strip of one batch: the fused kernel writes gradWeight itself (no reduction kernel, no
+    workspace). The same values as batch 0 of a two-batch problem whose batch 1 has gradY = 0 (so
+    adds nothing) run the two-kernel path with the same per-column sums: gradX of batch 0 and
+    gradWeight must be the same bits."""
+    H = 448
+    one = custom(S, 1, H, dtype, mask, seed=S + 1)
+    assert mdc.mccb_get_workspace_size(S, 1, H, mdc.DTYPE_CODE[torch.bfloat16]) == 0
+    assert mdc.mccb_get_workspace_size(S, 2, H, mdc.DTYPE_CODE[torch.bfloat16]) > 0
+    gy, x, w, m = gpu_inputs(one)
+    gy2 = torch.cat([gy, torch.zeros_like(gy)], dim=1).contiguous()
+    x2 = torch.cat([x, x.flip(0)], dim=1).contiguous()
+    m2 = None if m is None else torch.cat([m, torch.ones_like(m)], dim=0).contiguous()
+    announce(f"direct path S={S} B=1 {dtype}")
+    gx1, gw1 = mdc.backward(gy, x, w, m)
+    announce(f"two-kernel path S={S} B=2 {dtype}")
+    gx2, gw2 = mdc.backward(gy2, x2, w, m2)
+    torch.cuda.synchronize()
+    assert torch.equal(gw1.view(torch.int16), gw2.view(torch.int16))
+    assert torch.equal(gx1[:, 0].view(torch.int16), gx2[:, 0].view(torch.int16))
+    compare_full(one, gx1, gw1, tag=f"direct S={S}")
