@@ -184,7 +184,9 @@ struct FusedCfg {
     static constexpr int BW = CG * RG;         // waves per block
     static constexpr int RR = RG * kTurnRows;  // rows a block advances per round
     // longest strip a block of this layout walks (the mask staging is unrolled for it)
-    static constexpr int MAX_STRIP = TALL ? kTallRows : kPlanMaxStripRows;
+    static constexpr int MAX_STRIP = TALL ? kTallRows
+                                     : LAYOUT == kLayoutNarrowRing ? (int)MCCB_MIN_STRIP_ROWS
+                                                                   : kPlanMaxStripRows;
     // column groups spaced this many lane vectors apart (0: adjacent)
     static constexpr int64_t DLV = WIDE ? (int64_t)MCCB_GROUP_SPACING / (V * 2) : 0;
     static_assert(!WIDE || W <= 3, "the wide layout holds at most 3 taps of fp64 state");
@@ -669,42 +671,78 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         __builtin_amdgcn_s_barrier();
     };
 
+    // A turn that may reach past the tensor's last row S-1 (its loads clamped there): the rows past
+    // S-1 are cleared (the staged mask already holds 0 for them) and only rows inside the strip
+    // are stored; its x rows past S-1 meet only cleared gradY rows and add nothing to gradWeight.
+    auto turn_clear = [&](int64_t i0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
+        uint32_t mw[4];
+        turn_mask(i0, mw);
+        if constexpr (!HAS_MASK) {
+            const int64_t nv = S - i0;  // rows of the turn that exist, >= 1
+            const uint64_t lo = nv >= 8 ? ~0ull : (1ull << (8 * nv)) - 1u;
+            const uint64_t hi = nv >= 16 ? ~0ull : nv <= 8 ? 0ull : (1ull << (8 * (nv - 8))) - 1u;
+            mw[0] = (uint32_t)lo;
+            mw[1] = (uint32_t)(lo >> 32);
+            mw[2] = (uint32_t)hi;
+            mw[3] = (uint32_t)(hi >> 32);
+        }
+        auto clear = [&](const vec_t &q, int k) -> vec_t {
+            const uint32_t m = (uint32_t)((int32_t)(mw[k >> 2] << (24 - 8 * (k & 3))) >> 24);
+            vec_t r;
+#pragma unroll
+            for (int p = 0; p < V / 2; ++p) r[p] = q[p] & m;
+            return r;
+        };
+        double d[W][V];
+#pragma unroll
+        for (int k = 0; k < L; ++k) widen<DT, V>(clear(qy[k], k), d[k]);
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+            widen<DT, V>(clear(qy[u + L], u + L), d[L]);
+            vec_t r;
+            if constexpr (VARLEN) {
+                const int lim = lim_of(i0 + u);
+                if (lim >= W)
+                    r = stencil_row<DT, W, V>(d, qx[u], wt, a);
+                else
+                    r = stencil_row<DT, W, V, true>(d, qx[u], wt, a, lim);
+            } else {
+                r = stencil_row<DT, W, V>(d, qx[u], wt, a);
+            }
+            if (active && i0 + u < rs1) store_vec(out_at(i0 + u), r);
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
+        }
+    };
     if constexpr (Cfg::TALL) {
-        // One round covers the strip. A turn that reaches past row S-1 clears the rows past it
-        // (the staged mask already holds 0 there) and stores only rows inside the strip; its x
-        // rows past S-1 meet only cleared gradY rows and add nothing to gradWeight.
-        if (t_i0 < rs1) {
-            uint32_t mw[4];
-            turn_mask(t_i0, mw);
-            if constexpr (!HAS_MASK) {
-                const int64_t nv = S - t_i0;  // rows of the turn that exist, >= 1
-                const uint64_t lo = nv >= 8 ? ~0ull : (1ull << (8 * nv)) - 1u;
-                const uint64_t hi = nv >= 16 ? ~0ull : nv <= 8 ? 0ull : (1ull << (8 * (nv - 8))) - 1u;
-                mw[0] = (uint32_t)lo;
-                mw[1] = (uint32_t)(lo >> 32);
-                mw[2] = (uint32_t)hi;
-                mw[3] = (uint32_t)(hi >> 32);
+        // one round covers the strip
+        if (t_i0 < rs1) turn_clear(t_i0, ty, tx);
+    } else if constexpr (LAYOUT == kLayoutNarrowRing) {
+        // Small grids: every turn's loads are clamped (a scalar operation per row), so the last
+        // strip's last turns need no separate, slower form; with a mask every turn takes the
+        // clearing form (one copy of the turn code keeps the registers in bounds).
+        auto has_turn = [&](int64_t r0) { return r0 + ring * TR < rs1; };
+        auto round_c = [&](int64_t r0, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR],
+                           vec_t (&ny)[TR + L], vec_t (&nx)[TR]) {
+            const int64_t rn = r0 + RR;
+            if (has_turn(rn)) issue_rows(std::true_type{}, rn + ring * TR, ny, nx);
+            if (has_turn(r0)) {
+                const int64_t i0 = r0 + ring * TR;
+                if (HAS_MASK || i0 + TR + L > S)
+                    turn_clear(i0, cy, cx);
+                else
+                    compute(r0, cy, cx);
             }
-            auto clear = [&](const vec_t &q, int k) -> vec_t {
-                const uint32_t m = (uint32_t)((int32_t)(mw[k >> 2] << (24 - 8 * (k & 3))) >> 24);
-                vec_t r;
-#pragma unroll
-                for (int p = 0; p < V / 2; ++p) r[p] = q[p] & m;
-                return r;
-            };
-            double d[W][V];
-#pragma unroll
-            for (int k = 0; k < L; ++k) widen<DT, V>(clear(ty[k], k), d[k]);
-#pragma unroll
-            for (int u = 0; u < TR; ++u) {
-                widen<DT, V>(clear(ty[u + L], u + L), d[L]);
-                const vec_t r = stencil_row<DT, W, V>(d, tx[u], wt, a);
-                if (active && t_i0 + u < rs1) store_vec(out_at(t_i0 + u), r);
-#pragma unroll
-                for (int k = 0; k < L; ++k)
-#pragma unroll
-                    for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
-            }
+            __builtin_amdgcn_s_barrier();  // as in round() below
+        };
+        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        if (has_turn(rs0)) issue_rows(std::true_type{}, rs0 + ring * TR, ay, ax);
+        for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
+            round_c(r0, ay, ax, by, bx);
+            if (r0 + RR >= rs1) break;
+            round_c(r0 + RR, by, bx, ay, ax);
         }
     } else {
         vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
@@ -1239,6 +1277,7 @@ hipError_t launch_fused(const Plan &p, const void *gy, const void *x, const void
     // the kernel's assumptions: turns never straddle an inner strip end, the tall layout has one
     // strip, and a direct gradWeight write needs the in-block sum over several ring waves
     if ((!Cfg::TALL && p.rows_per_strip % Cfg::RR != 0) || (Cfg::TALL && p.n_strips != 1) ||
+        p.rows_per_strip > Cfg::MAX_STRIP ||
         (gw_direct && Cfg::RG < 2))
         return hipErrorInvalidValue;
     const FusedGrid fg = fused_grid<TAPS, T, LAYOUT>(p.C);
