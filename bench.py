@@ -245,7 +245,9 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
                                           "frac": round(pct(k1_alg, k1_avg) / 100, 4),
                                           "traffic": measured_traffic(
                                               wlc.name, traffic_file("mccb_fused_bwd", wlc.name))},
-                         "reduce_kernel_avg_ms": round(k2_ms / max(n_prof, 1), 5),
+                         # no reduction kernel runs when the fused kernel writes gradWeight
+                         "reduce_kernel_avg_ms": (None if direct
+                                                  else round(k2_ms / max(n_prof, 1), 5)),
                          "flat_stream": {"median_ms": round(s_med, 5),
                                          "pct_of_hbm_peak": pct(s_alg, s_med),
                                          "backward_pct_of_flat_stream": round(
