@@ -412,6 +412,11 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     typedef typename Vec<V>::t vec_t;
     constexpr int L = W - 1;  // look-ahead rows
     extern __shared__ __attribute__((aligned(16))) uint8_t smask[];
+    // Whether a wave's turns overlap (the next turn's loads in flight while the current turn is
+    // computed; see issue_sel). Measured per layout: the plain ring (a padded tensor, many blocks
+    // of adjacent column groups with two ring waves each) runs faster without, every other layout
+    // with.
+    constexpr bool kPipe = LAYOUT != kLayoutRing || VARLEN;
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane of a wave; saying so keeps everything derived from
@@ -474,6 +479,40 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         for (int u = TR - L; u < TR; ++u) qy[u + L] = load_vec_cached(at_gy(row(i0 + L + u)));
 #pragma unroll
         for (int u = 0; u < TR; ++u) qx[u] = load_vec(at_x(row(i0 + u)));
+    };
+    // Every round issues one turn of loads, with no condition around them: behind a condition the
+    // compiler's wait counts before each row of the current turn must also hold on the path
+    // without those loads, so on the path with them each row would wait for the next turn's loads
+    // as well and the two turns would not overlap. Without a next turn (`real` false, the same on
+    // every lane) the loads read the first row of the weights, which is in L2, and are not used.
+    const uint32_t w_lane = (uint32_t)(h * 2);
+    auto issue_sel = [&](auto clamp_tag, bool real, int64_t i0, vec_t(&qy)[TR + L],
+                         vec_t(&qx)[TR]) {
+        constexpr bool CLAMP = decltype(clamp_tag)::value;
+        const int s1 = (int)(S - 1);  // rows are below 2^31
+        auto row = [&](int r) -> int {
+            if constexpr (CLAMP) return r < s1 ? r : s1;
+            return r;
+        };
+        const int r0 = (int)i0;
+        const char *gb = real ? gy_base : reinterpret_cast<const char *>(w_);
+        const char *xb = real ? x_base : reinterpret_cast<const char *>(w_);
+        const int64_t grb = real ? gy_rb : 0, xrb = real ? x_rb : 0;
+        const uint32_t gl = real ? gy_lane : w_lane, xl = real ? x_lane : w_lane;
+        auto gy_at = [&](int r) {
+            return reinterpret_cast<const vec_t *>(gb + (int64_t)row(r) * grb + gl);
+        };
+        auto x_at = [&](int r) {
+            return reinterpret_cast<const vec_t *>(xb + (int64_t)row(r) * xrb + xl);
+        };
+#pragma unroll
+        for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(gy_at(r0 + k));
+#pragma unroll
+        for (int u = 0; u < TR - L; ++u) qy[u + L] = load_gy_stream(gy_at(r0 + L + u));
+#pragma unroll
+        for (int u = TR - L; u < TR; ++u) qy[u + L] = load_vec_cached(gy_at(r0 + L + u));
+#pragma unroll
+        for (int u = 0; u < TR; ++u) qx[u] = load_vec(x_at(r0 + u));
     };
     // The tall layout's blocks live a single round: each wave's one turn (clamped near the end of
     // the tensor) goes out before the mask staging, so that one round trip covers both.
@@ -594,8 +633,14 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 
     // A turn is "whole" when this wave's TR rows and their look-ahead rows all exist.
     auto whole = [&](int64_t r0) {
-        const int64_t i0 = r0 + ring * TR;
-        return i0 + TR <= rs1 && i0 + TR + L <= S;
+        if constexpr (kPipe) {
+            // rows are below 2^31: 32-bit compares stay in scalar registers
+            const int i0 = (int)r0 + ring * TR;
+            return i0 + TR <= (int)rs1 && i0 + TR + L <= (int)S;
+        } else {
+            const int64_t i0 = r0 + ring * TR;
+            return i0 + TR <= rs1 && i0 + TR + L <= S;
+        }
     };
     // Issue the loads of a whole turn: gradY rows i0 .. i0+TR+L-1 and x rows i0 .. i0+TR-1. The
     // first L gradY rows were the previous turn's last look-ahead rows (this wave's own with one
@@ -723,26 +768,59 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         // Small grids: every turn's loads are clamped (a scalar operation per row), so the last
         // strip's last turns need no separate, slower form; with a mask every turn takes the
         // clearing form (one copy of the turn code keeps the registers in bounds).
-        auto has_turn = [&](int64_t r0) { return r0 + ring * TR < rs1; };
-        auto round_c = [&](int64_t r0, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR],
-                           vec_t (&ny)[TR + L], vec_t (&nx)[TR]) {
-            const int64_t rn = r0 + RR;
-            if (has_turn(rn)) issue_rows(std::true_type{}, rn + ring * TR, ny, nx);
-            if (has_turn(r0)) {
-                const int64_t i0 = r0 + ring * TR;
-                if (HAS_MASK || i0 + TR + L > S)
-                    turn_clear(i0, cy, cx);
-                else
-                    compute(r0, cy, cx);
-            }
-            __builtin_amdgcn_s_barrier();  // as in round() below
+        auto has_turn = [&](int r0) { return r0 + ring * TR < (int)rs1; };
+        auto turn_c = [&](int r0, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR]) {
+            const int64_t i0 = r0 + ring * TR;
+            if (HAS_MASK || i0 + TR + L > S)
+                turn_clear(i0, cy, cx);
+            else
+                compute(r0, cy, cx);
         };
+        // The rounds in which this wave has a turn come first (a turn exists while its first row
+        // is inside the strip); every round loads the next turn (see issue_sel) and computes
+        // this one, with no other path through the loop, so the compiler's wait counts are
+        // exact. Unrolled by two so that the two register buffers swap roles without copies.
+        // Then one barrier for each round left (every wave passes one barrier per round).
         vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
-        if (has_turn(rs0)) issue_rows(std::true_type{}, rs0 + ring * TR, ay, ax);
-        for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
-            round_c(r0, ay, ax, by, bx);
-            if (r0 + RR >= rs1) break;
-            round_c(r0 + RR, by, bx, ay, ax);
+        int r0 = (int)rs0;
+        issue_sel(std::true_type{}, has_turn(r0), r0 + ring * TR, ay, ax);
+        for (; has_turn(r0); r0 += 2 * RR) {
+            issue_sel(std::true_type{}, has_turn(r0 + RR), r0 + RR + ring * TR, by, bx);
+            turn_c(r0, ay, ax);
+            __builtin_amdgcn_s_barrier();  // as in round()
+            if (!has_turn(r0 + RR)) {
+                r0 += RR;
+                break;
+            }
+            issue_sel(std::true_type{}, has_turn(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax);
+            turn_c(r0 + RR, by, bx);
+            __builtin_amdgcn_s_barrier();
+        }
+        for (; r0 < (int)rs1; r0 += RR) __builtin_amdgcn_s_barrier();
+    } else if constexpr (kPipe) {
+        // As in the narrow ring: first the rounds in which this wave's turn is whole, each loading
+        // the next turn and computing this one with no other path through the loop, then the rest
+        // of the strip (the last strip's turns that reach past row S-1, or none) row by row, one
+        // barrier per round.
+        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        auto next_whole = [&](int r) { return r < (int)rs1 && whole(r); };
+        int r0 = (int)rs0;
+        issue_sel(std::false_type{}, whole(r0), r0 + ring * TR, ay, ax);
+        for (; whole(r0); r0 += 2 * RR) {
+            issue_sel(std::false_type{}, next_whole(r0 + RR), r0 + RR + ring * TR, by, bx);
+            compute(r0, ay, ax);
+            __builtin_amdgcn_s_barrier();  // as in round()
+            if (!next_whole(r0 + RR)) {
+                r0 += RR;
+                break;
+            }
+            issue_sel(std::false_type{}, next_whole(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax);
+            compute(r0 + RR, by, bx);
+            __builtin_amdgcn_s_barrier();
+        }
+        for (; r0 < (int)rs1; r0 += RR) {
+            partial(r0);
+            __builtin_amdgcn_s_barrier();
         }
     } else {
         vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
