@@ -514,12 +514,35 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 #pragma unroll
         for (int u = 0; u < TR; ++u) qx[u] = load_vec(x_at(r0 + u));
     };
-    // The tall layout's blocks live a single round: each wave's one turn (clamped near the end of
-    // the tensor) goes out before the mask staging, so that one round trip covers both.
-    vec_t ty[TR + L], tx[TR];
+    // A turn is "whole" when this wave's TR rows and their look-ahead rows all exist.
+    auto whole = [&](int64_t r0) {
+        if constexpr (kPipe) {
+            // rows are below 2^31: 32-bit compares stay in scalar registers
+            const int i0 = (int)r0 + ring * TR;
+            return i0 + TR <= (int)rs1 && i0 + TR + L <= (int)S;
+        } else {
+            const int64_t i0 = r0 + ring * TR;
+            return i0 + TR <= rs1 && i0 + TR + L <= S;
+        }
+    };
+    // Whether this wave has a turn in the round that starts at row r0 (its first row inside the
+    // strip).
+    auto has_turn = [&](int r0) { return r0 + ring * TR < (int)rs1; };
+    // The weights and the first turn's loads go out before the mask staging (every layout but the
+    // plain ring), so that one round trip covers all three at the start of a block.
+    const vec_t *w = reinterpret_cast<const vec_t *>(w_);
+    vec_t ay[TR + L], ax[TR], wraw[W];
     const int64_t t_i0 = rs0 + ring * TR;
-    if constexpr (Cfg::TALL) {
-        if (t_i0 < rs1) issue_rows(std::true_type{}, t_i0, ty, tx);
+    if constexpr (kPipe) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) wraw[k] = w[(k * H + h) / V];
+        if constexpr (Cfg::TALL) {
+            if (t_i0 < rs1) issue_rows(std::true_type{}, t_i0, ay, ax);
+        } else if constexpr (LAYOUT == kLayoutNarrowRing) {
+            issue_sel(std::true_type{}, has_turn((int)rs0), t_i0, ay, ax);
+        } else {
+            issue_sel(std::false_type{}, whole(rs0), t_i0, ay, ax);
+        }
     }
 
     int moff = 0;  // offset of this lane's batch in the staged mask
@@ -584,12 +607,11 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         return W;
     };
 
-    const vec_t *w = reinterpret_cast<const vec_t *>(w_);
     double wt[W][V];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         float t[V];
-        unpack_vec<DT, V>(w[(k * H + h) / V], t);
+        unpack_vec<DT, V>(kPipe ? wraw[k] : w[(k * H + h) / V], t);
 #pragma unroll
         for (int e = 0; e < V; ++e) wt[k][e] = (double)t[e];
     }
@@ -631,17 +653,6 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         return r;
     };
 
-    // A turn is "whole" when this wave's TR rows and their look-ahead rows all exist.
-    auto whole = [&](int64_t r0) {
-        if constexpr (kPipe) {
-            // rows are below 2^31: 32-bit compares stay in scalar registers
-            const int i0 = (int)r0 + ring * TR;
-            return i0 + TR <= (int)rs1 && i0 + TR + L <= (int)S;
-        } else {
-            const int64_t i0 = r0 + ring * TR;
-            return i0 + TR <= rs1 && i0 + TR + L <= S;
-        }
-    };
     // Issue the loads of a whole turn: gradY rows i0 .. i0+TR+L-1 and x rows i0 .. i0+TR-1. The
     // first L gradY rows were the previous turn's last look-ahead rows (this wave's own with one
     // wave per group, the other ring wave's otherwise), and this turn's last L are the next turn's
@@ -763,12 +774,11 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     };
     if constexpr (Cfg::TALL) {
         // one round covers the strip
-        if (t_i0 < rs1) turn_clear(t_i0, ty, tx);
+        if (t_i0 < rs1) turn_clear(t_i0, ay, ax);
     } else if constexpr (LAYOUT == kLayoutNarrowRing) {
         // Small grids: every turn's loads are clamped (a scalar operation per row), so the last
         // strip's last turns need no separate, slower form; with a mask every turn takes the
         // clearing form (one copy of the turn code keeps the registers in bounds).
-        auto has_turn = [&](int r0) { return r0 + ring * TR < (int)rs1; };
         auto turn_c = [&](int r0, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR]) {
             const int64_t i0 = r0 + ring * TR;
             if (HAS_MASK || i0 + TR + L > S)
@@ -781,9 +791,8 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         // this one, with no other path through the loop, so the compiler's wait counts are
         // exact. Unrolled by two so that the two register buffers swap roles without copies.
         // Then one barrier for each round left (every wave passes one barrier per round).
-        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        vec_t by[TR + L], bx[TR];
         int r0 = (int)rs0;
-        issue_sel(std::true_type{}, has_turn(r0), r0 + ring * TR, ay, ax);
         for (; has_turn(r0); r0 += 2 * RR) {
             issue_sel(std::true_type{}, has_turn(r0 + RR), r0 + RR + ring * TR, by, bx);
             turn_c(r0, ay, ax);
@@ -802,10 +811,9 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         // the next turn and computing this one with no other path through the loop, then the rest
         // of the strip (the last strip's turns that reach past row S-1, or none) row by row, one
         // barrier per round.
-        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        vec_t by[TR + L], bx[TR];
         auto next_whole = [&](int r) { return r < (int)rs1 && whole(r); };
         int r0 = (int)rs0;
-        issue_sel(std::false_type{}, whole(r0), r0 + ring * TR, ay, ax);
         for (; whole(r0); r0 += 2 * RR) {
             issue_sel(std::false_type{}, next_whole(r0 + RR), r0 + RR + ring * TR, by, bx);
             compute(r0, ay, ax);
@@ -823,7 +831,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
             __builtin_amdgcn_s_barrier();
         }
     } else {
-        vec_t ay[TR + L], ax[TR], by[TR + L], bx[TR];
+        vec_t by[TR + L], bx[TR];
         if (whole(rs0)) issue(rs0, ay, ax);
         // Unrolled by two so that the two register buffers swap roles without copies.
         for (int64_t r0 = rs0; r0 < rs1; r0 += 2 * RR) {
