@@ -18,9 +18,10 @@
 // Kernel 1 (fused): the rows are cut into strips and the columns into blocks; a block walks its
 // strip down the rows, a wavefront holding one wave-wide load (64 lanes x V columns, a "column
 // group") of each row it handles. Two lane layouts, chosen from the shape alone:
-//   wide (windows of up to 3 taps, B*H a multiple of 32768): 8-byte lanes, 4 column groups per
-//     block placed 16 KiB apart in the row, one wave per group. Four wave-wide loads that far apart
-//     are served faster by the HBM than four adjacent ones.
+//   wide (windows of up to 3 taps, B*H at least 32768): 8-byte lanes, 4 column groups per block
+//     placed 16 KiB apart in the row (adjacent in a row's last, partial 64 KiB), one wave per
+//     group. Four wave-wide loads that far apart are served faster by the HBM than four adjacent
+//     ones.
 //   ring (everything else): 4-byte lanes, column groups of adjacent columns with 2 waves each,
 //     which take the strip's rows round robin; 4 groups per block, or 2 (the narrow ring) where
 //     the plan's grid would otherwise stay small (a column's sums do not depend on the count).
@@ -159,8 +160,9 @@ struct Vec {
 
 // Lane layouts of the fused kernel (all give each column's gradX bit for bit; gradWeight's fp64
 // partials are summed in the layout's order, and the layout is a function of the shape only):
-//   WIDE (windows of up to 3 taps, rows a whole number of super-chunks): 8-byte lanes, a block is
-//        4 column groups spaced MCCB_GROUP_SPACING bytes apart, one wave per group;
+//   WIDE (windows of up to 3 taps, rows of at least one super-chunk): 8-byte lanes, a block is
+//        4 column groups spaced MCCB_GROUP_SPACING bytes apart (adjacent past the row's last whole
+//        super-chunk), one wave per group;
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
 //        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
 //        4-tap windows).
@@ -1327,11 +1329,12 @@ FusedGrid fused_grid(int64_t C) {
 }
 
 // The wide layout is used for windows of up to 3 taps (padded layouts) when a row of B*H columns
-// is a whole number of its super-chunks (CG groups x the group spacing); elsewhere the ring layout.
-// A function of the shape only, so gradWeight's summation order is too.
+// holds at least one of its super-chunks (CG groups x the group spacing: 32768 columns); the rest
+// of such a row takes blocks of adjacent groups. Elsewhere the ring layouts. A function of the
+// shape only, so gradWeight's summation order is too.
 bool fused_wide(int64_t C, int64_t W) {
     typedef FusedCfg<3, false, kLayoutWide> Cfg;
-    return W <= 3 && Cfg::DLV > 0 && (C / Cfg::V) % (Cfg::CG * Cfg::DLV) == 0;
+    return W <= 3 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV);
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).

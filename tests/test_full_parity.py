@@ -98,17 +98,21 @@ def test_whole_workload(idx):
         st.release()
 
 
-def test_whole_four_group_ring_masked():
-    """A masked shape on the 4-group ring (512 columns per block), whose column groups straddle
-    batch boundaries (H = 3904 is not a multiple of 512), compared whole; then the same values
-    stored [B,S,H] and read in place through their strides, which runs 2 column groups per block:
-    the column groups of a block enter no column's summation order, so both outputs must be the
-    same bits."""
+@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 17, 3904, 1024, 65)],
+                         ids=["four_group_ring", "wide_partial_super_chunk"])
+def test_whole_masked_layouts(S, B, H, cols, ncb):
+    """Masked shapes compared whole, on two layouts whose column groups straddle batch boundaries
+    (H = 3904 is not a multiple of a group's columns): the 4-group ring (512 columns per block),
+    and the wide layout on a row of 2 whole 64 KiB super-chunks plus a partial one, whose last
+    block places its groups side by side. Then the same values stored [B,S,H] and read in place
+    through their strides (on the ring shape this runs 2 column groups per block): the column
+    groups of a block enter no column's summation order, so both outputs must be the same
+    bits."""
     from synth import custom
 
-    wl = custom(2048, 17, 3904, "bf16", ("bernoulli", 0.85), seed=2048)
+    wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S + B)
     plan = mdc.mccb_get_plan(wl.S, wl.B, wl.H, mdc.MCCB_BF16)
-    assert plan["cols_per_block"] == 512 and plan["waves_per_block"] == 8, plan
+    assert plan["cols_per_block"] == cols and plan["n_col_blocks"] == ncb, plan
     st = Stream(wl)
     try:
         st.compare_rows(wl.S)
