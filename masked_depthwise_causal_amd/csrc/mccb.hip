@@ -428,8 +428,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     const int group = wave % CG;  // column group
     const int64_t C = B * H;
     const int64_t CV = C / V;  // lane vectors per row
-    const int64_t col_block = blockIdx.x % n_col_blocks;
-    const int64_t strip = blockIdx.x / n_col_blocks;
+    // (block, row and column indices are below 2^31: 32-bit divisions, a few instructions each
+    // instead of a 64-bit division's hundred)
+    const int64_t col_block = (int64_t)(blockIdx.x % (uint32_t)n_col_blocks);
+    const int64_t strip = (int64_t)(blockIdx.x / (uint32_t)n_col_blocks);
     const int64_t rs0 = strip * rows_per_strip;
     const int64_t rs1 = (rs0 + rows_per_strip < S) ? rs0 + rows_per_strip : S;
 
@@ -439,9 +441,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     const bool active = v_raw < CV;
     const int64_t v = active ? v_raw : CV - 1;
     const int64_t c = v * V;
-    const int64_t j = c / H;
+    const int64_t j = (int64_t)((uint32_t)c / (uint32_t)H);
     const int64_t h = c - j * H;
-    const int64_t jg = ((v0 < CV ? v0 : CV - 1) * V) / H;  // the wave's first batch
+    // the wave's first batch
+    const int64_t jg = (int64_t)((uint32_t)((v0 < CV ? v0 : CV - 1) * V) / (uint32_t)H);
 
     const int span = (int)(rows_per_strip + L);  // rows of the strip and its look-ahead
     const int mspan = (int)(rows_per_strip + kMaskPad);  // bytes of one staged mask slot
@@ -563,8 +566,8 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         for (int gg = 0; gg < CG; ++gg) {
             const int64_t vg = group_first_vec<CG>(col_block, gg, n_sp_blocks, Cfg::DLV);
             const int64_t va = vg < CV ? vg : CV - 1, vb = vg + kWave - 1 < CV ? vg + kWave - 1 : CV - 1;
-            jf[gg] = (va * V) / H;
-            two[gg] = (vb * V + V - 1) / H != jf[gg];
+            jf[gg] = (int64_t)((uint32_t)(va * V) / (uint32_t)H);
+            two[gg] = (int64_t)((uint32_t)(vb * V + V - 1) / (uint32_t)H) != jf[gg];
         }
         // Slot (gg, b) holds bytes rs0 .. rs0+mspan-1 of mask row jf[gg] + b; a thread takes bytes
         // tid, tid + kThreads, ... of every slot. The slot's batch is the same for the whole block.
@@ -916,8 +919,9 @@ __global__ void __launch_bounds__(kReduceWaves *kWave)
     constexpr int kBatch = 16;
     rvec_t acc = {};
     if (h < H && lo < hi) {
-        int64_t jj = lo % B;
-        int64_t off = ((lo / B) * W + k) * C + jj * H;
+        // (lo and B are below 2^31: 32-bit division)
+        int64_t jj = (int64_t)((uint32_t)lo % (uint32_t)B);
+        int64_t off = ((int64_t)((uint32_t)lo / (uint32_t)B) * W + k) * C + jj * H;
         const int64_t wrap = W * C - (B - 1) * H;  // from (s, B-1) to (s+1, 0)
         const double *base = ws + h;
         for (int64_t r = lo; r < hi; r += kBatch) {
@@ -1008,8 +1012,10 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     constexpr int L = W - 1;  // look-back rows
     extern __shared__ uint8_t fwd_reserved[];  // sized at launch, never used: caps blocks per CU
     if (S < 0) fwd_reserved[threadIdx.x] = 0;   // never taken (S >= 1): keeps the symbol live
-    const int64_t ct = blockIdx.x % n_ct;  // column tile (fastest)
-    const int64_t rt = blockIdx.x / n_ct;  // row tile
+    // (tile, column and batch indices are below 2^31: 32-bit divisions, a few instructions each
+    // instead of a 64-bit division's hundred)
+    const int64_t ct = (int64_t)(blockIdx.x % (uint32_t)n_ct);  // column tile (fastest)
+    const int64_t rt = (int64_t)(blockIdx.x / (uint32_t)n_ct);  // row tile
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wc = wave & ((1 << cw_log2) - 1), wr = wave >> cw_log2;  // column slot, row slot
@@ -1018,8 +1024,9 @@ __global__ void __launch_bounds__(kFwdWaves *kWave)
     if (c0 >= C) return;  // no barrier below: lanes past the last column just leave
     const int64_t CV = C / kFwdVec;  // lane vectors per row (C is a multiple of 64)
     const int64_t v = c0 / kFwdVec;
-    const int64_t h0 = c0 % H;  // the lane's kFwdVec channels share one batch: H % 64 == 0
-    const int64_t j = c0 / H;
+    // the lane's kFwdVec channels share one batch: H % 64 == 0
+    const int64_t j = (int64_t)((uint32_t)c0 / (uint32_t)H);
+    const int64_t h0 = c0 - j * H;
     const int64_t r0 = (rt * (kFwdWaves >> cw_log2) + wr) * kFwdRows;  // may be >= S: rows guarded
 
     // Loads are issued before any of them is used, weights first (the first rows' arithmetic
