@@ -178,8 +178,8 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
     """Backward and forward of every workload, each call timed on its own between HIP events,
     after reading a 1 GiB scratch buffer so that no input is left in the 256 MB Infinity Cache or
     the L2s (the small workloads would otherwise run from cache). The flush reads rather than
-    writes, so no dirty lines are left to be written back during the timed call. Median and
-    minimum.
+    writes, so no dirty lines are left to be written back during the timed call. Each series
+    starts with 10 untimed calls. Median and minimum.
 
     For the backward a second pass of the same calls records the library's HIP events around its
     two kernels (mccb_profile_begin/_end): `fused_kernel` is the fused kernel's average duration
@@ -195,16 +195,20 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def per_call(fn):
+    def per_call(fn, warm=10):
+        # untimed calls first: a kernel's first calls after the inputs are generated or another
+        # kernel has run take up to 20 % longer, and settle after about ten
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
         times = []
-        for r in range(reps + 2):
+        for r in range(reps):
             flush.sum()
             e0.record(stream)
             fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            if r >= 2:
-                times.append(e0.elapsed_time(e1))
+            times.append(e0.elapsed_time(e1))
         return statistics.median(times), min(times)
 
     def pct(nbytes, ms):
@@ -223,8 +227,8 @@ def time_all_configs(torch, mdc, workloads, wls, dev, stream, reps: int) -> list
         b_med, b_min = per_call(bwd)
         # a second pass of the same per-call timing with the library's kernel events on (they add
         # their own time to the call, so the call's own figure comes from the pass above)
-        mdc.mccb_profile_begin(reps + 2)
-        per_call(bwd)
+        mdc.mccb_profile_begin(reps)
+        per_call(bwd, warm=0)
         k1_ms, k2_ms, n_prof = mdc.mccb_profile_end()
         f_med, f_min = per_call(lambda: mdc.forward(x_c, w_c, m_c, y=y_c, stream=stream))
         s_med, _ = per_call(lambda: torch.add(gy_c, x_c, out=gx_c))

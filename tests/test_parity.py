@@ -162,3 +162,42 @@ def test_direct_gradweight_equals_two_kernel_path(S, dtype, mask):
     assert torch.equal(gw1.view(torch.int16), gw2.view(torch.int16))
     assert torch.equal(gx1[:, 0].view(torch.int16), gx2[:, 0].view(torch.int16))
     compare_full(one, gx1, gw1, tag=f"direct S={S}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_gradx_double_rounding_cases(dtype):
+    """gradX sums built to sit just beside a midpoint between two neighbouring values of the
+    format, closer than fp32 resolves: rounding to fp32 first lands exactly on the midpoint, and a
+    second round-to-nearest-even would then go the wrong way for sums just above it. Compared with
+    the oracle's correctly rounded values, and checked against the expected bits directly."""
+    import oracle
+
+    orc = oracle.get()
+    S, B, H = 4, 1, 384
+    # the sum at row 0 is gy0*w2 + gy1*w1 + gy2*w0 = 1 + half an ulp of the format at 1 + d
+    half = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    tiny, wscale = (2.0 ** -40, 1.0) if dtype == "bf16" else (2.0 ** -20, 2.0 ** -20)
+    gy = np.zeros((S, B, H))
+    w = np.ones((3, H))
+    sign = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)      # the sum's sign
+    d_sign = np.where(np.arange(H) % 4 < 2, 1.0, -1.0)     # d above or below the midpoint
+    d_zero = np.arange(H) % 8 == 7                         # d = 0: an exact midpoint
+    gy[0, 0] = sign
+    gy[1, 0] = sign * half
+    gy[2, 0] = np.where(d_zero, 0.0, sign * d_sign * tiny)
+    w[0] = wscale  # gy2 meets w[0]
+    x = np.ones((S, B, H))
+    gy16, x16, w16 = (orc.encode(dtype, a) for a in (gy, x, w))
+    assert np.array_equal(orc.decode(dtype, gy16), gy) and np.array_equal(orc.decode(dtype, w16), w)
+    acc = np.zeros((3, H))
+    ref = orc.backward_rows(dtype, S, 0, S, gy16, x16, w16, None, acc)
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    up = np.where(d_zero, one, np.where(d_sign > 0, one + 1, one))  # magnitude bits of row 0
+    assert np.array_equal(ref[0, 0] & 0x7FFF, up.astype(np.uint16))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    to_dev = lambda a: torch.from_numpy(a.astype(np.int16)).view(tdt).to("cuda")  # noqa: E731
+    announce(f"mccb_backward double-rounding cases {dtype}")
+    gx, _ = mdc.backward(to_dev(gy16), to_dev(x16), to_dev(w16), None)
+    torch.cuda.synchronize()
+    got = gx.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} gradX elements differ"
