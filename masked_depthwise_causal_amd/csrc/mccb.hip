@@ -18,7 +18,7 @@
 // Kernel 1 (fused): the rows are cut into strips and the columns into blocks; a block walks its
 // strip down the rows, a wavefront holding one wave-wide load (64 lanes x V columns, a "column
 // group") of each row it handles. Two lane layouts, chosen from the shape alone:
-//   wide (windows of up to 3 taps, B*H at least 32768): 8-byte lanes, 4 column groups per block
+//   wide (B*H at least 32768): 8-byte lanes, 4 column groups per block
 //     placed 16 KiB apart in the row (adjacent in a row's last, partial 64 KiB), one wave per
 //     group. Four wave-wide loads that far apart are served faster by the HBM than four adjacent
 //     ones.
@@ -160,12 +160,12 @@ struct Vec {
 
 // Lane layouts of the fused kernel (all give each column's gradX bit for bit; gradWeight's fp64
 // partials are summed in the layout's order, and the layout is a function of the shape only):
-//   WIDE (windows of up to 3 taps, rows of at least one super-chunk): 8-byte lanes, a block is
+//   WIDE (rows of at least one super-chunk): 8-byte lanes, a block is
 //        4 column groups spaced MCCB_GROUP_SPACING bytes apart (adjacent past the row's last whole
 //        super-chunk), one wave per group;
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
 //        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
-//        4-tap windows).
+//        4-tap windows). The wide layout's 4-tap window keeps fp32 weights widened per use.
 constexpr int kLayoutRing = 0, kLayoutWide = 1, kLayoutNarrowRing = 2, kLayoutTall = 3;
 // The tall layout (sequences of at most kTallRows rows, one strip): 8 ring waves on one column group
 // take every row of the strip in a single round, so a block's loads all go out together.
@@ -191,7 +191,7 @@ struct FusedCfg {
                                                                    : kPlanMaxStripRows;
     // column groups spaced this many lane vectors apart (0: adjacent)
     static constexpr int64_t DLV = WIDE ? (int64_t)MCCB_GROUP_SPACING / (V * 2) : 0;
-    static_assert(!WIDE || W <= 3, "the wide layout holds at most 3 taps of fp64 state");
+    static_assert(!WIDE || W <= 4, "the wide layout holds at most 4 taps");
     static_assert(V == 2 || V == 4, "lane vector must be 4 or 8 bytes");
     static_assert(GC < 384, "a column group spans at most 2 batches (H >= 384)");
     static_assert(CG <= 8, "the staged mask holds two batches for each of at most 8 groups");
@@ -310,10 +310,10 @@ __device__ static inline void store_vec(T *p, T v) {
 // gYm[i+k]), and the gradWeight terms of row i: a[k] += gYm[i+W-1-k] * x[i]. Returns the packed
 // gradX row. LIMITED (packed variable-length layout): only d[k] with k < lim belong to row i's
 // sequence; the rest count as zero.
-template <int DT, int W, int V, bool LIMITED = false>
+template <int DT, int W, int V, bool LIMITED = false, typename WT = double>
 __device__ static inline typename Vec<V>::t stencil_row(const double (&d)[W][V],
                                                        const typename Vec<V>::t x_row,
-                                                       const double (&wt)[W][V],
+                                                       const WT (&wt)[W][V],
                                                        double (&a)[W][V], int lim = W) {
     float xf[V];
     unpack_vec<DT, V>(x_row, xf);
@@ -321,10 +321,10 @@ __device__ static inline typename Vec<V>::t stencil_row(const double (&d)[W][V],
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         // gradX[i] = sum_k gYm[i+k] * w[W-1-k], in k order (each product exact in fp64)
-        double s = d[0][e] * wt[W - 1][e];
+        double s = d[0][e] * (double)wt[W - 1][e];
 #pragma unroll
         for (int k = 1; k < W; ++k)
-            s = __builtin_fma((!LIMITED || k < lim) ? d[k][e] : 0.0, wt[W - 1 - k][e], s);
+            s = __builtin_fma((!LIMITED || k < lim) ? d[k][e] : 0.0, (double)wt[W - 1 - k][e], s);
 #if MCCB_EXACT_GRADX
         out[e] = round_to_odd_f32(s);
 #else
@@ -612,14 +612,28 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         return W;
     };
 
-    double wt[W][V];
+    // The wide layout's 4-tap window keeps its weights in fp32 (exact for 16-bit values) and
+    // widens them at each use: fp64 copies of 4 taps x 4 columns would not fit beside its state.
+    constexpr bool kNarrowW = Cfg::WIDE && W > 3;
+    typedef typename std::conditional<kNarrowW, float, double>::type wt_t;
+    wt_t wt[W][V];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         float t[V];
         unpack_vec<DT, V>(kPipe ? wraw[k] : w[(k * H + h) / V], t);
 #pragma unroll
-        for (int e = 0; e < V; ++e) wt[k][e] = (double)t[e];
+        for (int e = 0; e < V; ++e) wt[k][e] = (wt_t)t[e];
     }
+    // an empty asm that "changes" the fp32 weights each row, so that their widening is redone at
+    // the use instead of being hoisted into fp64 copies that live through the loop
+    auto refresh_wt = [&]() {
+        if constexpr (kNarrowW) {
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) asm volatile("" : "+v"(wt[k][e]));
+        }
+    };
 
     double a[W][V];
 #pragma unroll
@@ -677,6 +691,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
             widen<DT, V>(masked(qy[u + L], mw, u + L), d[L]);
+            refresh_wt();
             vec_t r;
             if constexpr (VARLEN) {
                 // a uniform branch: only the last W-1 rows of a sequence take the limited form
@@ -707,6 +722,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
             widen<DT, V>((i0 + k < S && keep(i0 + k)) ? load_vec_cached(at_gy(i0 + k)) : zero, d[k]);
         for (int64_t i = i0; i < i1; ++i) {
             widen<DT, V>((i + L < S && keep(i + L)) ? load_vec_cached(at_gy(i + L)) : zero, d[L]);
+            refresh_wt();
             const vec_t r = VARLEN ? stencil_row<DT, W, V, true>(d, load_vec(at_x(i)), wt, a, lim_of(i))
                                    : stencil_row<DT, W, V>(d, load_vec(at_x(i)), wt, a);
             if (active) store_vec(out_at(i), r);
@@ -760,6 +776,7 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
             widen<DT, V>(clear(qy[u + L], u + L), d[L]);
+            refresh_wt();
             vec_t r;
             if constexpr (VARLEN) {
                 const int lim = lim_of(i0 + u);
@@ -1335,13 +1352,13 @@ FusedGrid fused_grid(int64_t C) {
     return g;
 }
 
-// The wide layout is used for windows of up to 3 taps (padded layouts) when a row of B*H columns
+// The wide layout is used for the padded layouts (windows of 1..4 taps) when a row of B*H columns
 // holds at least one of its super-chunks (CG groups x the group spacing: 32768 columns); the rest
 // of such a row takes blocks of adjacent groups. Elsewhere the ring layouts. A function of the
 // shape only, so gradWeight's summation order is too.
 bool fused_wide(int64_t C, int64_t W) {
     typedef FusedCfg<3, false, kLayoutWide> Cfg;
-    return W <= 3 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV);
+    return W <= 4 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV);
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).
@@ -1394,7 +1411,7 @@ hipError_t launch_fused_layout(int layout, const Plan &p, const void *gy, const 
             return launch_fused<DT, M, T, TAPS, VL, kLayoutTall>(p, gy, x, w, mask, gx, ws, st,
                                                                  lds, is, ahead, lim_lds, gw_direct);
     }
-    if constexpr (TAPS <= 3 && !VL) {
+    if constexpr (!VL) {
         if (layout == kLayoutWide)
             return launch_fused<DT, M, T, TAPS, VL, kLayoutWide>(p, gy, x, w, mask, gx, ws, st,
                                                                  lds, is, ahead, lim_lds, gw_direct);

@@ -324,8 +324,8 @@ def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
 
 
 def test_ex_lane_width_decides_in_place_reads():
-    """The in-place rule follows the fused kernel's lane width: 8 bytes on shapes with S > 64,
-    W <= 3 and B*H at least 32768, 4 bytes elsewhere. Even strides and a 4-byte (not 8-byte)
+    """The in-place rule follows the fused kernel's lane width: 8 bytes on shapes with S > 64 and
+    B*H at least 32768, 4 bytes elsewhere. Even strides and a 4-byte (not 8-byte)
     aligned base are read in place on a 4-byte-lane shape and packed on an 8-byte-lane shape."""
     for S, B, H, wide in [(128, 8, 4096, True), (128, 12, 4096, True), (64, 8, 4096, False),
                           (128, 3, 4096, False), (128, 7, 4672, False)]:
@@ -338,9 +338,10 @@ def test_ex_lane_width_decides_in_place_reads():
         st = strides(S, B, H, gy=[B * (H + 2), H + 2, 1])
         got = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 3, BF16, st)
         assert got == (packed if wide else base), (S, B, H)
-        # W = 4 never takes the 8-byte lanes
+        # W = 4 takes the same lanes (the workspace holds 4 taps of partials)
+        base4 = mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 4, BF16, None)
         got = mdc.mccb_get_workspace_size_ex(gy4, X, W, S, B, H, 4, BF16, None)
-        assert got == mdc.mccb_get_workspace_size_ex(GY, X, W, S, B, H, 4, BF16, None)
+        assert got == (-(-base4 // 256) * 256 + nb if wide else base4), (S, B, H)
 
 
 @pytest.mark.parametrize("which", ["gy", "x", "w", "gx", "gw"])
