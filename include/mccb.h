@@ -169,7 +169,7 @@ typedef struct {
  * contiguous (H stride 1), its row and batch strides are multiples of the fused kernel's lane
  * width in elements, its base is aligned to the lane width in bytes, and a wave's columns span
  * less than 4 GiB of it. The lane width is 8 bytes (4 elements) on shapes with S > 64 and B*H at
- * least 32768, and 4 bytes (2 elements) on all others. Any other gradY or x is first
+ * least 32768 and a multiple of 4096, and 4 bytes (2 elements) on all others. Any other gradY or x is first
  * packed into a contiguous copy inside the workspace (one extra read and write of that tensor),
  * and a weight that is not contiguous and 16-byte aligned is packed too; phase 1 includes those
  * copies in the size it reports. The mask is read through its strides. Phase 1 therefore takes the input pointers as well (as the page's

@@ -18,7 +18,7 @@
 // Kernel 1 (fused): the rows are cut into strips and the columns into blocks; a block walks its
 // strip down the rows, a wavefront holding one wave-wide load (64 lanes x V columns, a "column
 // group") of each row it handles. Two lane layouts, chosen from the shape alone:
-//   wide (B*H at least 32768): 8-byte lanes, 4 column groups per block
+//   wide (B*H at least 32768, a multiple of 4096): 8-byte lanes, 4 column groups per block
 //     placed 16 KiB apart in the row (adjacent in a row's last, partial 64 KiB), one wave per
 //     group. Four wave-wide loads that far apart are served faster by the HBM than four adjacent
 //     ones.
@@ -160,7 +160,7 @@ struct Vec {
 
 // Lane layouts of the fused kernel (all give each column's gradX bit for bit; gradWeight's fp64
 // partials are summed in the layout's order, and the layout is a function of the shape only):
-//   WIDE (rows of at least one super-chunk): 8-byte lanes, a block is
+//   WIDE (rows of at least one super-chunk, a multiple of 4096 columns): 8-byte lanes, a block is
 //        4 column groups spaced MCCB_GROUP_SPACING bytes apart (adjacent past the row's last whole
 //        super-chunk), one wave per group;
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
@@ -1353,12 +1353,14 @@ FusedGrid fused_grid(int64_t C) {
 }
 
 // The wide layout is used for the padded layouts (windows of 1..4 taps) when a row of B*H columns
-// holds at least one of its super-chunks (CG groups x the group spacing: 32768 columns); the rest
-// of such a row takes blocks of adjacent groups. Elsewhere the ring layouts. A function of the
-// shape only, so gradWeight's summation order is too.
+// holds at least one of its super-chunks (CG groups x the group spacing: 32768 columns) and is a
+// whole number of 4096 columns (8 KiB); the rest of such a row takes blocks of adjacent groups.
+// Elsewhere the ring layouts. (Measured: on rows 6 KiB past a multiple of 8 KiB the ring is
+// 4 points faster, on rows a multiple of 8 KiB the wide layout is 2-8 points faster.) A function
+// of the shape only, so gradWeight's summation order is too.
 bool fused_wide(int64_t C, int64_t W) {
     typedef FusedCfg<3, false, kLayoutWide> Cfg;
-    return W <= 4 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV);
+    return W <= 4 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV) && C % 4096 == 0;
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).

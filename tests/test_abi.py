@@ -325,10 +325,11 @@ def test_ex_workspace_packs_only_what_cannot_be_read_in_place():
 
 def test_ex_lane_width_decides_in_place_reads():
     """The in-place rule follows the fused kernel's lane width: 8 bytes on shapes with S > 64 and
-    B*H at least 32768, 4 bytes elsewhere. Even strides and a 4-byte (not 8-byte)
+    B*H at least 32768 and a multiple of 4096, 4 bytes elsewhere. Even strides and a 4-byte (not 8-byte)
     aligned base are read in place on a 4-byte-lane shape and packed on an 8-byte-lane shape."""
     for S, B, H, wide in [(128, 8, 4096, True), (128, 12, 4096, True), (64, 8, 4096, False),
-                          (128, 3, 4096, False), (128, 7, 4672, False)]:
+                          (128, 3, 4096, False), (128, 7, 4672, False), (128, 7, 5120, False),
+                          (128, 32, 1152, True)]:
         base, nb = _ws(S, B, H), S * B * H * 2
         packed = -(-base // 256) * 256 + nb
         gy4 = GY + 4  # 4-byte aligned, not 8

@@ -98,13 +98,13 @@ def test_whole_workload(idx):
         st.release()
 
 
-@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 17, 3904, 1024, 65)],
+@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 32, 1152, 1024, 36)],
                          ids=["four_group_ring", "wide_partial_super_chunk"])
 def test_whole_masked_layouts(S, B, H, cols, ncb):
     """Masked shapes compared whole, on two layouts whose column groups straddle batch boundaries
-    (H = 3904 is not a multiple of a group's columns): the 4-group ring (512 columns per block),
-    and the wide layout on a row of 2 whole 64 KiB super-chunks plus a partial one, whose last
-    block places its groups side by side. Then the same values stored [B,S,H] and read in place
+    (H is not a multiple of a group's columns): the 4-group ring (512 columns per block), and the
+    wide layout on a row of one whole 64 KiB super-chunk plus a partial one, whose last blocks
+    place their groups side by side. Then the same values stored [B,S,H] and read in place
     through their strides (on the ring shape this runs 2 column groups per block): the column
     groups of a block enter no column's summation order, so both outputs must be the same
     bits."""
