@@ -98,16 +98,18 @@ def test_whole_workload(idx):
         st.release()
 
 
-@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 32, 1152, 1024, 36)],
-                         ids=["four_group_ring", "wide_partial_super_chunk"])
+@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 32, 1152, 1024, 36),
+                                             (1360, 24, 2048, 768, 64)],
+                         ids=["four_group_ring", "wide_partial_super_chunk", "three_group_wide"])
 def test_whole_masked_layouts(S, B, H, cols, ncb):
-    """Masked shapes compared whole, on two layouts whose column groups straddle batch boundaries
-    (H is not a multiple of a group's columns): the 4-group ring (512 columns per block), and the
-    wide layout on a row of one whole 64 KiB super-chunk plus a partial one, whose last blocks
-    place their groups side by side. Then the same values stored [B,S,H] and read in place
-    through their strides (on the ring shape this runs 2 column groups per block): the column
-    groups of a block enter no column's summation order, so both outputs must be the same
-    bits."""
+    """Masked shapes compared whole, on three layouts: the 4-group ring (512 columns per block)
+    and the wide layout on a row of one whole 64 KiB super-chunk plus a partial one, whose last
+    blocks place their groups side by side, both with column groups that straddle batch
+    boundaries (H is not a multiple of a group's columns); and the 3-group wide layout on 96 KiB
+    rows (groups 32 KiB apart, 16 batches per super-chunk). Then the same values stored [B,S,H]
+    and read in place through their strides (on the ring shape this runs 2 column groups per
+    block, on the 96 KiB rows the 4-group wide layout): the column groups of a block enter no
+    column's summation order, so both outputs must be the same bits."""
     from synth import custom
 
     wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S + B)

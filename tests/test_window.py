@@ -87,6 +87,17 @@ def test_strided_inputs_with_w4():
     fwd_compare_full(wl, y, tag="W=4 strided")
 
 
+@pytest.mark.parametrize("W", [2, 4])
+def test_three_group_wide_windows(W):
+    """Rows of 96 KiB take the wide layout with 3 column groups 32 KiB apart (768 columns per
+    block); 2 and 4 taps compared whole, S with a ragged last round."""
+    wl = custom(203, 24, 2048, "bf16", ("bernoulli", 0.85), seed=203 + W, W=W)
+    plan = plan_of(wl)
+    assert plan["cols_per_block"] == 768 and plan["waves_per_block"] == 3, plan
+    gx, gw = gpu_run(wl, poison_workspace=True)
+    compare_full(wl, gx, gw, tag=f"W={W} 3-group wide")
+
+
 @pytest.mark.parametrize("W,idx", [(2, 3), (4, 3), (4, 4), (1, 2)],
                          ids=lambda v: str(v))
 def test_full_size_window_sampled(W, idx):
