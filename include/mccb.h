@@ -235,7 +235,7 @@ int mccb_varlen_forward(const void *x, const void *weight, const uint8_t *mask,
                         int64_t W, int dtype, void *workspace, uint64_t workspace_size,
                         void *stream);
 
-/* The tiling chosen for a shape, for mccb_backward (first eight fields) and mccb_forward (fwd_*);
+/* The tiling chosen for a shape, for mccb_backward (fwd_* excepted) and mccb_forward (fwd_*);
  * a pure function of (S, B, H, dtype). Exposed so that tests can place edge cases on tile
  * boundaries. */
 typedef struct {
@@ -251,6 +251,8 @@ typedef struct {
     int64_t fwd_cols_per_tile; /* columns of [S, B*H] one mccb_forward block covers */
     int64_t fwd_n_col_tiles;   /* ceil(B*H / fwd_cols_per_tile) */
     int64_t fwd_n_row_tiles;   /* ceil(S / fwd_rows_per_tile) */
+    int64_t group_spacing;     /* bytes between the column groups of a fused-kernel block
+                                  (0: adjacent groups) */
 } mccb_plan_t;
 
 /* Fills *plan for a valid shape. Same return codes as mccb_get_workspace_size. Host-only. */

@@ -22,7 +22,8 @@ class Plan(ctypes.Structure):
                 ("n_col_blocks", ctypes.c_int64), ("waves_per_block", ctypes.c_int64),
                 ("workspace_size", ctypes.c_uint64),
                 ("fwd_rows_per_tile", ctypes.c_int64), ("fwd_cols_per_tile", ctypes.c_int64),
-                ("fwd_n_col_tiles", ctypes.c_int64), ("fwd_n_row_tiles", ctypes.c_int64)]
+                ("fwd_n_col_tiles", ctypes.c_int64), ("fwd_n_row_tiles", ctypes.c_int64),
+                ("group_spacing", ctypes.c_int64)]
 
 
 class Strides(ctypes.Structure):

@@ -163,26 +163,28 @@ struct Vec {
 //   WIDE (rows of at least one super-chunk, a multiple of 4096 columns): 8-byte lanes, a block is
 //        4 column groups spaced MCCB_GROUP_SPACING bytes apart (adjacent past the row's last whole
 //        super-chunk), one wave per group;
-//   WIDE3 (rows a whole number of 96 KiB and not of 64 KiB): the same with 3 column groups
-//        32 KiB apart, so a 96 KiB super-chunk tiles the row;
+//        Two more spacings, for rows the 64 KiB super-chunk tiles an even number of times or
+//        not at all: 4 groups 32 KiB apart (128 KiB super-chunks) and 3 groups 32 KiB apart
+//        (96 KiB);
 //   ring: 4-byte lanes, a block is column groups of adjacent columns with 2 ring waves each
 //        (fewer groups, one wave less per SIMD, when the registers run short: strided 3-tap and
 //        4-tap windows). The wide layout's 4-tap window keeps fp32 weights widened per use.
 constexpr int kLayoutRing = 0, kLayoutWide = 1, kLayoutNarrowRing = 2, kLayoutTall = 3,
-              kLayoutWide3 = 4;
-// group spacing of the 3-group wide layout, in bytes
-constexpr int64_t kWide3Spacing = 32768;
+              kLayoutWide4x32 = 4, kLayoutWide3x32 = 5;
+// group spacing of the two other wide layouts, in bytes
+constexpr int64_t kWide32Spacing = 32768;
 // The tall layout (sequences of at most kTallRows rows, one strip): 8 ring waves on one column group
 // take every row of the strip in a single round, so a block's loads all go out together.
 constexpr int kTallWaves = 8;
 constexpr int kTallRows = kTallWaves * kTurnRows;
 template <int W, bool STRIDED, int LAYOUT>
 struct FusedCfg {
-    static constexpr bool WIDE = LAYOUT == kLayoutWide || LAYOUT == kLayoutWide3;
+    static constexpr bool WIDE =
+        LAYOUT == kLayoutWide || LAYOUT == kLayoutWide4x32 || LAYOUT == kLayoutWide3x32;
     static constexpr bool TALL = LAYOUT == kLayoutTall;
     static constexpr bool tight = (STRIDED && W >= 3) || W > 3;
     static constexpr int V = WIDE ? MCCB_WIDE_VEC : 2;  // columns per lane
-    static constexpr int CG = LAYOUT == kLayoutWide3 ? 3
+    static constexpr int CG = LAYOUT == kLayoutWide3x32 ? 3
                               : WIDE ? MCCB_WIDE_COL_GROUPS
                               : TALL ? 1
                                      : ((tight || LAYOUT == kLayoutNarrowRing) ? 2 : MCCB_RING_COL_GROUPS);
@@ -196,9 +198,10 @@ struct FusedCfg {
                                      : LAYOUT == kLayoutNarrowRing ? (int)MCCB_MIN_STRIP_ROWS
                                                                    : kPlanMaxStripRows;
     // column groups spaced this many lane vectors apart (0: adjacent)
-    static constexpr int64_t DLV = LAYOUT == kLayoutWide3 ? kWide3Spacing / (V * 2)
-                                   : WIDE                   ? (int64_t)MCCB_GROUP_SPACING / (V * 2)
-                                                            : 0;
+    static constexpr int64_t DLV =
+        (LAYOUT == kLayoutWide4x32 || LAYOUT == kLayoutWide3x32) ? kWide32Spacing / (V * 2)
+        : WIDE                                                   ? (int64_t)MCCB_GROUP_SPACING / (V * 2)
+                                                                 : 0;
     static_assert(!WIDE || W <= 4, "the wide layout holds at most 4 taps");
     static_assert(V == 2 || V == 4, "lane vector must be 4 or 8 bytes");
     static_assert(GC < 384, "a column group spans at most 2 batches (H >= 384)");
@@ -1371,17 +1374,23 @@ bool fused_wide(int64_t C, int64_t W) {
     return W <= 4 && Cfg::DLV > 0 && (C / Cfg::V) >= (Cfg::CG * Cfg::DLV) && C % 4096 == 0;
 }
 
-// Among the wide rows, those a whole number of the 3-group layout's 96 KiB super-chunks and not
-// of the 4-group layout's 64 KiB ones take the 3-group layout, so that no block is left with
-// adjacent groups. Measured per row length (3-tap bf16 backward, % of 8 TB/s, 4 groups -> 3):
-// 96 KiB 70.4 -> 74.0, 288 KiB 70.7 -> 71.4, 480 KiB 71.2 -> 71.5; on rows a whole number of
-// 64 KiB the 4-group layout stays ahead (128 KiB 74.7 -> 70.0, 320 KiB 75.4 -> 69.0). Contiguous
-// inputs only: the row length is the memory's. Groups enter no column's summation order, so the
-// results equal the 4-group layout's bit for bit.
-bool fused_wide3(int64_t C, int64_t W, bool strided) {
-    typedef FusedCfg<3, false, kLayoutWide3> Cfg;
-    const int64_t super_cols = Cfg::CG * Cfg::DLV * Cfg::V;  // 49152 columns: 96 KiB
-    return !strided && fused_wide(C, W) && C % super_cols == 0 && C % 32768 != 0;
+// Which wide layout a row takes: the one whose super-chunk (groups x spacing) tiles the row an odd
+// number of times, in the order 4 x 16 KiB, 4 x 32 KiB, 3 x 32 KiB; else 4 x 16 KiB with blocks of
+// adjacent groups in the row's last, partial super-chunk. Measured per row length (3-tap bf16
+// backward, % of 8 TB/s, alternating runs): an even number of super-chunks, or a partial one,
+// costs 1-7 points against an odd number (4 x 16 KiB on 128 KiB rows 70.3-71.8 against 4 x 32 KiB
+// 72.9-73.4; 3 x 16 KiB on 96 KiB rows 67 against 3 x 32 KiB 74.0 and 4 x 16 KiB 70.4; 3 x 32 KiB
+// on 192 KiB rows 72.2 against 4 x 16 KiB 74.5; 4 x 32 KiB on 384 and 640 KiB rows +0.7-0.8).
+// Rows a whole number of 256 KiB have no odd tiling here and keep 4 x 16 KiB (ahead of 4 x 32 KiB
+// on 1536 KiB rows by 0.5). Contiguous inputs only: the row length is the memory's. Groups enter
+// no column's summation order, so every wide layout gives the same bits.
+int wide_layout(int64_t C, bool strided) {
+    const int64_t L = C * 2;  // bytes of a row
+    const int64_t K = 1024;
+    if (strided || (L % (64 * K) == 0 && (L / (64 * K)) % 2 == 1)) return kLayoutWide;
+    if (L % (128 * K) == 0 && (L / (128 * K)) % 2 == 1) return kLayoutWide4x32;
+    if (L % (96 * K) == 0 && (L / (96 * K)) % 2 == 1) return kLayoutWide3x32;
+    return kLayoutWide;
 }
 
 // Columns per lane of the fused kernel that a call runs (its loads' size and alignment).
@@ -1398,8 +1407,7 @@ int fused_vec(int64_t S, int64_t C, int64_t W) {
 // order, so the narrow ring's results equal the ring's bit for bit.
 int fused_layout(const Plan &p, bool strided, bool varlen) {
     if (!varlen && p.S <= kTallRows) return kLayoutTall;  // one strip, one round
-    if (!varlen && fused_wide(p.C, p.W))
-        return fused_wide3(p.C, p.W, strided) ? kLayoutWide3 : kLayoutWide;
+    if (!varlen && fused_wide(p.C, p.W)) return wide_layout(p.C, strided);
     const bool tight = (strided && p.W >= 3) || p.W > 3;
     if (!tight && fused_grid<3, false, kLayoutRing>(p.C).ncb * p.n_strips < kMinBlocks)
         return kLayoutNarrowRing;
@@ -1441,9 +1449,12 @@ hipError_t launch_fused_layout(int layout, const Plan &p, const void *gy, const 
                                                                  lds, is, ahead, lim_lds, gw_direct);
     }
     if constexpr (!VL && !T) {
-        if (layout == kLayoutWide3)
-            return launch_fused<DT, M, T, TAPS, VL, kLayoutWide3>(p, gy, x, w, mask, gx, ws, st,
-                                                                  lds, is, ahead, lim_lds, gw_direct);
+        if (layout == kLayoutWide4x32)
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutWide4x32>(
+                p, gy, x, w, mask, gx, ws, st, lds, is, ahead, lim_lds, gw_direct);
+        if (layout == kLayoutWide3x32)
+            return launch_fused<DT, M, T, TAPS, VL, kLayoutWide3x32>(
+                p, gy, x, w, mask, gx, ws, st, lds, is, ahead, lim_lds, gw_direct);
     }
     if constexpr (!((T && TAPS >= 3) || TAPS > 3)) {  // instantiated where the ring is not narrow
         if (layout == kLayoutNarrowRing)
@@ -1849,6 +1860,17 @@ void *scratch_on(hipStream_t stream) {
     return g_scratch.ptr[dev];
 }
 
+// The fused kernel's block shape for a layout (the contiguous 3-tap launch).
+template <int LAYOUT>
+void fill_plan(const Plan &p, mccb_plan_t *plan) {
+    typedef FusedCfg<3, false, LAYOUT> Cfg;
+    plan->rows_per_round = Cfg::RR;
+    plan->cols_per_block = Cfg::CG * Cfg::GC;
+    plan->n_col_blocks = fused_grid<3, false, LAYOUT>(p.C).ncb;
+    plan->waves_per_block = Cfg::BW;
+    plan->group_spacing = Cfg::DLV * Cfg::V * 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1867,39 +1889,16 @@ int mccb_get_plan(int64_t S, int64_t B, int64_t H, int dtype, mccb_plan_t *plan)
     if (rc != MCCB_OK) return rc;
     const Plan p = make_plan(S, B, H, dtype);
     const int layout = fused_layout(p, false, false);  // the contiguous 3-tap launch
-    typedef FusedCfg<3, false, kLayoutWide> Wd;
-    typedef FusedCfg<3, false, kLayoutWide3> W3;
-    typedef FusedCfg<3, false, kLayoutRing> Rg;
-    typedef FusedCfg<3, false, kLayoutNarrowRing> Nr;
-    typedef FusedCfg<3, false, kLayoutTall> Tl;
     plan->rows_per_turn = kTurnRows;
     plan->rows_per_strip = p.rows_per_strip;
     plan->n_strips = p.n_strips;
-    if (layout == kLayoutTall) {
-        plan->rows_per_round = Tl::RR;
-        plan->cols_per_block = Tl::CG * Tl::GC;
-        plan->n_col_blocks = fused_grid<3, false, kLayoutTall>(p.C).ncb;
-        plan->waves_per_block = Tl::BW;
-    } else if (layout == kLayoutWide3) {
-        plan->rows_per_round = W3::RR;
-        plan->cols_per_block = W3::CG * W3::GC;
-        plan->n_col_blocks = fused_grid<3, false, kLayoutWide3>(p.C).ncb;
-        plan->waves_per_block = W3::BW;
-    } else if (layout == kLayoutWide) {
-        plan->rows_per_round = Wd::RR;
-        plan->cols_per_block = Wd::CG * Wd::GC;
-        plan->n_col_blocks = fused_grid<3, false, kLayoutWide>(p.C).ncb;
-        plan->waves_per_block = Wd::BW;
-    } else if (layout == kLayoutNarrowRing) {
-        plan->rows_per_round = Nr::RR;
-        plan->cols_per_block = Nr::CG * Nr::GC;
-        plan->n_col_blocks = fused_grid<3, false, kLayoutNarrowRing>(p.C).ncb;
-        plan->waves_per_block = Nr::BW;
-    } else {
-        plan->rows_per_round = Rg::RR;
-        plan->cols_per_block = Rg::CG * Rg::GC;
-        plan->n_col_blocks = fused_grid<3, false, kLayoutRing>(p.C).ncb;
-        plan->waves_per_block = Rg::BW;
+    switch (layout) {
+        case kLayoutTall: fill_plan<kLayoutTall>(p, plan); break;
+        case kLayoutWide: fill_plan<kLayoutWide>(p, plan); break;
+        case kLayoutWide4x32: fill_plan<kLayoutWide4x32>(p, plan); break;
+        case kLayoutWide3x32: fill_plan<kLayoutWide3x32>(p, plan); break;
+        case kLayoutNarrowRing: fill_plan<kLayoutNarrowRing>(p, plan); break;
+        default: fill_plan<kLayoutRing>(p, plan); break;
     }
     plan->workspace_size = p.ws_bytes;
     const FwdPlan f = make_fwd_plan(S, B, H);

@@ -234,6 +234,34 @@ def test_plan_is_pure_and_consistent():
         assert mdc.mccb_get_plan(S, B, H, other) == p1
 
 
+def test_wide_layout_tiles_rows_an_odd_number_of_times():
+    """The wide layouts (column groups 16 or 32 KiB apart) on every row length they cover: the
+    block's super-chunk (groups x spacing) fits a whole, odd number of times in a row, preferring
+    4 x 16 KiB, then 4 x 32 KiB, then 3 x 32 KiB; rows with no such tiling (a whole number of
+    256 KiB, or none of the three) take 4 x 16 KiB. Contiguous launches; the plan reports them."""
+    K = 1024
+    seen = set()
+    for C in range(32768, 786432 + 1, 4096):  # rows of 64 KiB .. 1.5 MiB, whole 8 KiB
+        B = next(b for b in range(1, 33) if C % b == 0 and C // b <= 24576 and (C // b) % 64 == 0)
+        p = mdc.mccb_get_plan(1024, B, C // B, BF16)
+        L = 2 * C
+        odd = [(g, sp) for g, sp in ((4, 16 * K), (4, 32 * K), (3, 32 * K))
+               if L % (g * sp) == 0 and (L // (g * sp)) % 2 == 1]
+        g, sp = odd[0] if odd else (4, 16 * K)
+        assert (p["waves_per_block"], p["group_spacing"], p["cols_per_block"]) == (g, sp, 256 * g), \
+            (C, B, p)
+        assert p["n_col_blocks"] == -(-C // p["cols_per_block"])
+        seen.add((g, sp, bool(odd)))
+    assert seen == {(4, 16 * K, True), (4, 32 * K, True), (3, 32 * K, True), (4, 16 * K, False)}
+    # the workloads' rows: 320 KiB -> 4 x 16, 128 KiB -> 4 x 32, 96 KiB -> 3 x 32; narrower rows
+    # take a ring layout (adjacent groups)
+    for (S, B, H, dt, sp, g) in [(16384, 32, 5120, BF16, 16 * K, 4), (8192, 8, 8192, FP16, 32 * K, 4),
+                                 (262144, 2, 24576, BF16, 32 * K, 3), (4096, 4, 4096, BF16, 0, 4),
+                                 (64, 1, 384, BF16, 0, 8)]:
+        p = mdc.mccb_get_plan(S, B, H, dt)
+        assert (p["group_spacing"], p["waves_per_block"]) == (sp, g), (S, B, H, p)
+
+
 # Strips of the fused kernel are at most this many rows: the plan aims for strips of 1024 rows and
 # the kernel's mask staging is sized for that bound (a whole number of 16-row rounds).
 MAX_STRIP_ROWS = 1024

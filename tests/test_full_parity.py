@@ -98,23 +98,27 @@ def test_whole_workload(idx):
         st.release()
 
 
-@pytest.mark.parametrize("S,B,H,cols,ncb", [(4352, 8, 3904, 512, 61), (2048, 32, 1152, 1024, 36),
-                                             (1360, 24, 2048, 768, 64)],
-                         ids=["four_group_ring", "wide_partial_super_chunk", "three_group_wide"])
-def test_whole_masked_layouts(S, B, H, cols, ncb):
-    """Masked shapes compared whole, on three layouts: the 4-group ring (512 columns per block)
+@pytest.mark.parametrize("S,B,H,cols,ncb,spacing",
+                         [(4352, 8, 3904, 512, 61, 0), (2048, 32, 1152, 1024, 36, 16384),
+                          (1360, 24, 2048, 768, 64, 32768), (1100, 32, 2048, 1024, 64, 32768)],
+                         ids=["four_group_ring", "wide_partial_super_chunk", "wide_3x32KiB",
+                              "wide_4x32KiB"])
+def test_whole_masked_layouts(S, B, H, cols, ncb, spacing):
+    """Masked shapes compared whole, on four layouts: the 4-group ring (512 columns per block)
     and the wide layout on a row of one whole 64 KiB super-chunk plus a partial one, whose last
     blocks place their groups side by side, both with column groups that straddle batch
-    boundaries (H is not a multiple of a group's columns); and the 3-group wide layout on 96 KiB
-    rows (groups 32 KiB apart, 16 batches per super-chunk). Then the same values stored [B,S,H]
-    and read in place through their strides (on the ring shape this runs 2 column groups per
-    block, on the 96 KiB rows the 4-group wide layout): the column groups of a block enter no
-    column's summation order, so both outputs must be the same bits."""
+    boundaries (H is not a multiple of a group's columns); the wide layout with 3 groups 32 KiB
+    apart on 96 KiB rows, and with 4 groups 32 KiB apart on 128 KiB rows (groups 16 batches
+    apart). Then the same values stored [B,S,H] and read in place through their strides (on the
+    ring shape this runs 2 column groups per block, on the last two the 4 x 16 KiB wide layout):
+    the column groups of a block enter no column's summation order, so both outputs must be the
+    same bits."""
     from synth import custom
 
     wl = custom(S, B, H, "bf16", ("bernoulli", 0.85), seed=S + B)
     plan = mdc.mccb_get_plan(wl.S, wl.B, wl.H, mdc.MCCB_BF16)
     assert plan["cols_per_block"] == cols and plan["n_col_blocks"] == ncb, plan
+    assert plan["group_spacing"] == spacing, plan
     st = Stream(wl)
     try:
         st.compare_rows(wl.S)

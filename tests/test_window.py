@@ -88,14 +88,16 @@ def test_strided_inputs_with_w4():
 
 
 @pytest.mark.parametrize("W", [2, 4])
-def test_three_group_wide_windows(W):
-    """Rows of 96 KiB take the wide layout with 3 column groups 32 KiB apart (768 columns per
-    block); 2 and 4 taps compared whole, S with a ragged last round."""
-    wl = custom(203, 24, 2048, "bf16", ("bernoulli", 0.85), seed=203 + W, W=W)
+@pytest.mark.parametrize("B,groups", [(24, 3), (32, 4)], ids=["96KiB_rows", "128KiB_rows"])
+def test_wide_32KiB_spacing_windows(W, B, groups):
+    """Rows of 96 and 128 KiB take the wide layout with column groups 32 KiB apart (3 and 4 groups
+    of 256 columns); 2 and 4 taps compared whole, S with a ragged last round."""
+    wl = custom(203, B, 2048, "bf16", ("bernoulli", 0.85), seed=203 + W + B, W=W)
     plan = plan_of(wl)
-    assert plan["cols_per_block"] == 768 and plan["waves_per_block"] == 3, plan
+    assert plan["cols_per_block"] == 256 * groups and plan["waves_per_block"] == groups, plan
+    assert plan["group_spacing"] == 32768, plan
     gx, gw = gpu_run(wl, poison_workspace=True)
-    compare_full(wl, gx, gw, tag=f"W={W} 3-group wide")
+    compare_full(wl, gx, gw, tag=f"W={W} wide {groups} x 32 KiB")
 
 
 @pytest.mark.parametrize("W,idx", [(2, 3), (4, 3), (4, 4), (1, 2)],
