@@ -312,12 +312,17 @@ __device__ static inline T load_fwd_stream(const T *p) {
 // base in scalar registers, so that the load or store takes the scalar-base + vector-offset form;
 // without it the compiler folds the loop-invariant lane offset into the base ahead of the loop and
 // forms every row's address with a 64-bit vector multiply-add. The base is cast back to the global
-// address space (the asm hides where it came from).
+// address space (the asm hides where it came from). Unoptimized device builds (the host-sanitizer
+// test) keep the plain sum: there the base is not kept uniform and cannot be pinned to SGPRs.
 template <typename P>
 __device__ static inline P *lane_at(P *row_base, uint32_t lane_off) {
+#if defined(__OPTIMIZE__)
     asm("" : "+s"(row_base));
     typedef __attribute__((address_space(1))) P gP;
     return (P *)((gP *)row_base + lane_off);
+#else
+    return row_base + lane_off;
+#endif
 }
 
 template <typename T>
