@@ -528,8 +528,9 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     // every lane) the loads read the first row of the weights, which is in L2, and are not used.
     const uint32_t w_lane = (uint32_t)(h * 2);
     auto issue_sel = [&](auto clamp_tag, bool real, int64_t i0, vec_t(&qy)[TR + L],
-                         vec_t(&qx)[TR]) {
+                         vec_t(&qx)[TR], auto lead_tag) {
         constexpr bool CLAMP = decltype(clamp_tag)::value;
+        constexpr bool LEAD = decltype(lead_tag)::value;  // the turn's first L gradY rows too
         const int s1 = (int)(S - 1);  // rows are below 2^31
         auto row = [&](int r) -> int {
             if constexpr (CLAMP) return r < s1 ? r : s1;
@@ -546,8 +547,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         auto x_at = [&](int r) {
             return reinterpret_cast<const vec_t *>(at_lane(xb + (int64_t)row(r) * xrb, xl));
         };
+        if constexpr (LEAD) {
 #pragma unroll
-        for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(gy_at(r0 + k));
+            for (int k = 0; k < L; ++k) qy[k] = load_vec_cached(gy_at(r0 + k));
+        }
 #pragma unroll
         for (int u = 0; u < TR - L; ++u) qy[u + L] = load_gy_stream(gy_at(r0 + L + u));
 #pragma unroll
@@ -580,9 +583,9 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         if constexpr (Cfg::TALL) {
             if (t_i0 < rs1) issue_rows(std::true_type{}, t_i0, ay, ax);
         } else if constexpr (LAYOUT == kLayoutNarrowRing) {
-            issue_sel(std::true_type{}, has_turn((int)rs0), t_i0, ay, ax);
+            issue_sel(std::true_type{}, has_turn((int)rs0), t_i0, ay, ax, std::true_type{});
         } else {
-            issue_sel(std::false_type{}, whole(rs0), t_i0, ay, ax);
+            issue_sel(std::false_type{}, whole(rs0), t_i0, ay, ax, std::true_type{});
         }
     }
 
@@ -720,13 +723,17 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     auto issue = [&](int64_t r0, vec_t (&qy)[TR + L], vec_t (&qx)[TR]) {
         issue_rows(std::false_type{}, r0 + ring * TR, qy, qx);
     };
-    auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
+    // A turn's rows; its fp64 window `d` either starts from the turn's first L gradY rows (LEAD)
+    // or holds them already: the wave's previous turn ends with exactly those rows in it.
+    auto compute_w = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR],
+                         double (&d)[W][V], auto lead_tag) {
         const int64_t i0 = r0 + ring * TR;
         uint32_t mw[4];
         turn_mask(i0, mw);
-        double d[W][V];
+        if constexpr (decltype(lead_tag)::value) {
 #pragma unroll
-        for (int k = 0; k < L; ++k) widen<DT, V>(masked(qy[k], mw, k), d[k]);
+            for (int k = 0; k < L; ++k) widen<DT, V>(masked(qy[k], mw, k), d[k]);
+        }
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
             widen<DT, V>(masked(qy[u + L], mw, u + L), d[L]);
@@ -748,6 +755,10 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
 #pragma unroll
                 for (int e = 0; e < V; ++e) d[k][e] = d[k + 1][e];
         }
+    };
+    auto compute = [&](int64_t r0, const vec_t (&qy)[TR + L], const vec_t (&qx)[TR]) {
+        double d[W][V];
+        compute_w(r0, qy, qx, d, std::true_type{});
     };
     // Partial turn at the end of the strip or of the tensor: one row at a time, gradY rows past S
     // read as zero.
@@ -855,14 +866,16 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         vec_t by[TR + L], bx[TR];
         int r0 = (int)rs0;
         for (; has_turn(r0); r0 += 2 * RR) {
-            issue_sel(std::true_type{}, has_turn(r0 + RR), r0 + RR + ring * TR, by, bx);
+            issue_sel(std::true_type{}, has_turn(r0 + RR), r0 + RR + ring * TR, by, bx,
+                      std::true_type{});
             turn_c(r0, ay, ax);
             __builtin_amdgcn_s_barrier();  // as in round()
             if (!has_turn(r0 + RR)) {
                 r0 += RR;
                 break;
             }
-            issue_sel(std::true_type{}, has_turn(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax);
+            issue_sel(std::true_type{}, has_turn(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax,
+                      std::true_type{});
             turn_c(r0 + RR, by, bx);
             __builtin_amdgcn_s_barrier();
         }
@@ -872,19 +885,40 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
         // the next turn and computing this one with no other path through the loop, then the rest
         // of the strip (the last strip's turns that reach past row S-1, or none) row by row, one
         // barrier per round.
+        // With one wave per column group (the wide layouts, up to 3 taps) a turn's first L gradY
+        // rows are the wave's previous turn's last ones: its fp64 window carries them over, and
+        // only the strip's first turn loads them (16 loads a turn instead of 18 at 3 taps).
+        constexpr bool kCarry = Cfg::RG == 1 && !VARLEN && W <= 3;
+        const auto lead = std::integral_constant<bool, !kCarry>{};
         vec_t by[TR + L], bx[TR];
+        double dc[W][V];  // the carried window (kCarry)
+        auto turn_w = [&](int r, const vec_t (&cy)[TR + L], const vec_t (&cx)[TR]) {
+            if constexpr (kCarry)
+                compute_w(r, cy, cx, dc, std::false_type{});
+            else
+                compute(r, cy, cx);
+        };
         auto next_whole = [&](int r) { return r < (int)rs1 && whole(r); };
         int r0 = (int)rs0;
+        if constexpr (kCarry) {
+            if (whole(r0)) {
+                uint32_t mw[4];
+                turn_mask(r0 + ring * TR, mw);
+#pragma unroll
+                for (int k = 0; k < L; ++k) widen<DT, V>(masked(ay[k], mw, k), dc[k]);
+            }
+        }
         for (; whole(r0); r0 += 2 * RR) {
-            issue_sel(std::false_type{}, next_whole(r0 + RR), r0 + RR + ring * TR, by, bx);
-            compute(r0, ay, ax);
+            issue_sel(std::false_type{}, next_whole(r0 + RR), r0 + RR + ring * TR, by, bx, lead);
+            turn_w(r0, ay, ax);
             __builtin_amdgcn_s_barrier();  // as in round()
             if (!next_whole(r0 + RR)) {
                 r0 += RR;
                 break;
             }
-            issue_sel(std::false_type{}, next_whole(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax);
-            compute(r0 + RR, by, bx);
+            issue_sel(std::false_type{}, next_whole(r0 + 2 * RR), r0 + 2 * RR + ring * TR, ay, ax,
+                      lead);
+            turn_w(r0 + RR, by, bx);
             __builtin_amdgcn_s_barrier();
         }
         for (; r0 < (int)rs1; r0 += RR) {
