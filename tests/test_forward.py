@@ -123,6 +123,10 @@ EDGE = [
     (33, 1, 5120, "bf16", ("bernoulli", 0.9)),
     (65, 1, 384, "bf16", ("prefix",)),
     (3, 1, 5120, "fp16", ("null",)),
+    # rows an odd number of 64 KiB (64, 192, 320 KiB): a block's 4 waves take chunks 16 KiB apart
+    (40, 8, 4096, "bf16", ("bernoulli", 0.8)),
+    (13, 6, 16384, "fp16", ("prefix",)),
+    (9, 32, 5120, "bf16", ("bernoulli", 0.9)),
 ]
 
 
