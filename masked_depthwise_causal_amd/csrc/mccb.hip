@@ -21,16 +21,18 @@
 //   wide (B*H at least 32768, a multiple of 4096): 8-byte lanes, 4 column groups per block
 //     placed 16 KiB apart in the row (adjacent in a row's last, partial 64 KiB), one wave per
 //     group. Four wave-wide loads that far apart are served faster by the HBM than four adjacent
-//     ones.
+//     ones, fastest when the block's super-chunk (groups x spacing) tiles the row an odd number
+//     of times: rows that 64 KiB does not tile so take 4 groups 32 KiB apart or 3 groups 32 KiB
+//     apart where those do.
 //   ring (everything else): 4-byte lanes, column groups of adjacent columns with 2 waves each,
 //     which take the strip's rows round robin; 4 groups per block, or 2 (the narrow ring) where
 //     the plan's grid would otherwise stay small (a column's sums do not depend on the count).
 // Either way a wave takes kTurnRows rows per round, and the block's waves pass a barrier each
 // round, so the block's loads of a row reach the HBM together; each row of gradY, x and gradX
 // crosses HBM once. A wave forms gradX for its kTurnRows rows from the masked gradY rows
-// i..i+kTurnRows+W-2 it holds in registers (the first W-1 are the previous turn's look-ahead rows,
-// loaded again and served from L2), and accumulates its gradWeight terms in fp64 across all its
-// rounds. Rounds are software-pipelined: a wave issues the loads of its next turn before computing
+// i..i+kTurnRows+W-2 it holds in registers (the first W-1 are the previous turn's look-ahead rows:
+// in the wide layout the same wave's, kept in its fp64 window; in the ring loaded again and served
+// from L2), and accumulates its gradWeight terms in fp64 across all its rounds. Rounds are software-pipelined: a wave issues the loads of its next turn before computing
 // the current one, so HBM requests stay in flight through the arithmetic and across the
 // (fence-free) round barrier. The strip's mask bytes are staged in LDS once. At the end each column
 // group writes one fp64 partial per (strip, tap, column) to the caller's workspace (the ring
@@ -666,8 +668,8 @@ __global__ void __launch_bounds__((FusedCfg<W, STRIDED, LAYOUT>::BW * kWave))
     // an empty asm that "changes" the fp32 weights, so that their widening is redone after it
     // instead of being hoisted into fp64 copies that live through the loop (which spills). Once
     // per whole turn: 4-tap headline backward 68.0-68.2 -> 72.1-72.2 % of 8 TB/s against once per
-    // row (70.4-70.5 every 2 rows, 71.7 every 4), 252 VGPRs and no spill; the row-at-a-time turns
-    // keep one per row.
+    // row (70.4-70.5 every 2 rows, 71.7 every 4), 249-256 VGPRs and no spill; the row-at-a-time
+    // turns keep one per row.
     auto refresh_wt = [&]() {
         if constexpr (kNarrowW) {
 #pragma unroll
