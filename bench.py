@@ -19,6 +19,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -277,6 +278,10 @@ def main() -> int:
                          "duration after about ten calls)")
     ap.add_argument("--workload", type=int, default=None,
                     help="index into synth.WORKLOADS (default: the B*S=512K H=5120 workload)")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="run the workload with this many rows S instead (same B, H, dtype and "
+                         "mask kind): a shorter stand-in for counter passes on inputs too large "
+                         "to generate under the profiler")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-single-seconds", type=float, default=1.5,
                     help="oracle time per workload for the single-thread samples (workloads 0-2)")
@@ -308,6 +313,8 @@ def main() -> int:
     from synth import workloads as wls
 
     wl = WORKLOADS[HEADLINE if args.workload is None else args.workload]
+    if args.rows is not None:
+        wl = dataclasses.replace(wl, S=args.rows, name=f"{wl.name}_rows{args.rows}")
     dev = torch.device("cuda:0")
     log(f"workload {wl.name}: {wl.describe()}")
     gy = wls.full_tensor(wl, wls.STREAM_GY, dev)
